@@ -1,0 +1,224 @@
+"""Benchmark of the blockwise-scaled FP8 linear-layer hot path on one MI355X.
+
+One step = one pass of the whole path over the full-layer workload at 16384 tokens
+(4 sequences of 4096), seed 0: for each of the 4 linear weights of one ~2B-scale layer
+(qkv 4096x2048, o 2048x2048, gate+up 12288x2048, down 2048x6144):
+    quantize W 128x128 (+ transposed copy), X 1x128, dY 1x128, dY 128x1, X 128x1;
+    FWD   Y  = X  W^T   (bf16 out)
+    DGRAD dX = dY W     (bf16 out)
+    WGRAD dW = dY^T X   (fp32 out)
+Inputs are seeded synthetic bf16 tensors already resident in HBM when timing starts.
+Prints ONE JSON line.  `value` = GEMM TFLOP/s of the whole step (all 12 GEMMs' flops
+divided by the step time, quantizers included in the time).
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA, TFLOP/s
+WORKLOAD = "layer_sweep_s0"
+METRIC = "FP8 blockwise GEMM TFLOP/s fwd/dgrad/wgrad (% FP8 MFMA peak); quant GB/s"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def build_step(P, torch, d):
+    """Allocate every buffer once; return the list of (kernel name, launch thunk, work dict)."""
+    from workloads import SWEEP_WEIGHTS
+    dev = "cuda:0"
+    ops = []
+
+    def bf16(b):
+        import numpy as np
+        return torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    u8 = lambda *s: torch.empty(s, dtype=torch.uint8, device=dev)
+    f32 = lambda *s: torch.empty(s, dtype=torch.float32, device=dev)
+    keep = []
+    for wname, (dout, din) in SWEEP_WEIGHTS:
+        X, W, dY = bf16(d[f"X_{wname}"]), bf16(d[f"W_{wname}"]), bf16(d[f"dY_{wname}"])
+        T = X.shape[0]
+        Wq, Ws, WqT, WsT = u8(dout, din), f32(dout // 128, din // 128), u8(din, dout), f32(din // 128, dout // 128)
+        Xq, Xs = u8(T, din), f32(din // 128, T)
+        Gq, Gs = u8(T, dout), f32(dout // 128, T)
+        GqT, GsT = u8(dout, T), f32(T // 128, dout)
+        XqT, XsT = u8(din, T), f32(T // 128, din)
+        Y = torch.empty((T, dout), dtype=torch.bfloat16, device=dev)
+        dX = torch.empty((T, din), dtype=torch.bfloat16, device=dev)
+        dW = f32(dout, din)
+        keep += [X, W, dY, Wq, Ws, WqT, WsT, Xq, Xs, Gq, Gs, GqT, GsT, XqT, XsT, Y, dX, dW]
+        qb = lambda n: {"kind": "quant", "bytes": 2 * n + n + 4 * (n // 128)}
+        qwb = {"kind": "quant", "bytes": 2 * dout * din + 2 * dout * din + 2 * 4 * (dout // 128) * (din // 128)}
+        gf = lambda m, n, k, ob: {"kind": "gemm", "flops": 2 * m * n * k, "bytes": m * k + n * k + 4 * (m + n) * (k // 128) + ob * m * n}
+        ops += [
+            ("quant_w_128x128", lambda W=W, Wq=Wq, Ws=Ws, WqT=WqT, WsT=WsT: P.puro_fp8_quant_w_128x128(W, Wq, Ws, WqT, WsT), qwb, wname),
+            ("quant_act_1x128", lambda X=X, Xq=Xq, Xs=Xs: P.puro_fp8_quant_act_1x128(X, Xq, Xs), qb(T * din), wname),
+            ("gemm_fwd", lambda Xq=Xq, Xs=Xs, Wq=Wq, Ws=Ws, Y=Y: P.puro_fp8_gemm(P.FWD, Xq, Xs, Wq, Ws, C=Y, out_dtype=P.OUT_BF16), gf(T, dout, din, 2), wname),
+            ("quant_act_1x128", lambda dY=dY, Gq=Gq, Gs=Gs: P.puro_fp8_quant_act_1x128(dY, Gq, Gs), qb(T * dout), wname),
+            ("gemm_dgrad", lambda Gq=Gq, Gs=Gs, WqT=WqT, WsT=WsT, dX=dX: P.puro_fp8_gemm(P.DGRAD, Gq, Gs, WqT, WsT, C=dX, out_dtype=P.OUT_BF16), gf(T, din, dout, 2), wname),
+            ("quant_act_128x1", lambda dY=dY, GqT=GqT, GsT=GsT: P.puro_fp8_quant_act_128x1(dY, GqT, GsT), qb(T * dout), wname),
+            ("quant_act_128x1", lambda X=X, XqT=XqT, XsT=XsT: P.puro_fp8_quant_act_128x1(X, XqT, XsT), qb(T * din), wname),
+            ("gemm_wgrad", lambda GqT=GqT, GsT=GsT, XqT=XqT, XsT=XsT, dW=dW: P.puro_fp8_gemm(P.WGRAD, GqT, GsT, XqT, XsT, C=dW, out_dtype=P.OUT_FP32), gf(dout, din, T, 4), wname),
+        ]
+    return ops, keep
+
+
+def cpu_baseline(d, tokens: int):
+    """The oracle, as it stands, on the first `tokens` tokens of the same step (all 4 weights)."""
+    import numpy as np
+    from oracle import gemm, quant
+    from workloads import SWEEP_WEIGHTS
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    flops = 0
+    t0 = time.perf_counter()
+    for wname, (dout, din) in SWEEP_WEIGHTS:
+        X = d[f"X_{wname}"][:tokens]
+        W = d[f"W_{wname}"]
+        dY = d[f"dY_{wname}"][:tokens]
+        Wq, Ws, WqT, WsT = quant.quant_w_128x128(W)
+        Xq, Xs = quant.quant_act_1x128(X)
+        gemm.gemm("FWD", Xq, Xs, Wq, Ws)
+        Gq, Gs = quant.quant_act_1x128(dY)
+        gemm.gemm("DGRAD", Gq, Gs, WqT, WsT)
+        GqT, GsT = quant.quant_act_128x1(dY)
+        XqT, XsT = quant.quant_act_128x1(X)
+        gemm.gemm("WGRAD", GqT, GsT, XqT, XsT)
+        flops += 3 * 2 * tokens * dout * din
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {tokens} of 16384 tokens of the same step (all 4 weights: full 128x128 weight "
+                      f"quantization, 1x128 and 128x1 activation/gradient quantization, float64 FWD/DGRAD/WGRAD); "
+                      f"{dt:.1f} s on {os.cpu_count()} host cpus",
+            "seconds": dt}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=512)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(data-parallel ranks would each run this same step on their own tokens)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import blockwise_scaled_fp8_quant_amd as P
+    from workloads import draw
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+
+    log("drawing inputs (layer sweep, 16384 tokens, seed 0) ...")
+    t0 = time.time()
+    d = draw(WORKLOAD)
+    log(f"  drawn in {time.time() - t0:.1f} s")
+    ops, keep = build_step(P, torch, d)
+    stream = torch.cuda.current_stream()
+
+    def step(events=None):
+        for i, (_, fn, _, _) in enumerate(ops):
+            if events is not None:
+                events[i][0].record(stream)
+            fn()
+            if events is not None:
+                events[i][1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup done ({args.warmup} steps); timing {args.steps} steps")
+
+    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in ops]
+          for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for k in range(args.steps):
+        step(ev[k])
+    stop.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    ms_per_step = total_ms / args.steps
+
+    # per-kernel durations (HIP events on the launch stream, inside the timed region)
+    per = {}
+    for k in range(args.steps):
+        for i, (name, _, work, wname) in enumerate(ops):
+            dt = ev[k][i][0].elapsed_time(ev[k][i][1])
+            e = per.setdefault(name, {"ms": [], "flops": 0, "bytes": 0, "launches": 0, "kind": work["kind"]})
+            e["ms"].append(dt)
+            e["launches"] += 1
+            e["flops"] += work.get("flops", 0)
+            e["bytes"] += work.get("bytes", 0)
+    kernels = {}
+    for name, e in per.items():
+        tot = sum(e["ms"])
+        avg = tot / len(e["ms"])
+        row = {"launches_per_step": e["launches"] // args.steps, "avg_us": round(1000 * avg, 2),
+               "share_of_step": round(tot / total_ms, 4)}
+        if e["kind"] == "gemm":
+            tf = e["flops"] / (tot / 1e3) / 1e12
+            row.update({"TFLOP/s": round(tf, 1), "frac_fp8_peak": round(tf / FP8_PEAK_TFLOPS, 4)})
+        else:
+            gbs = e["bytes"] / (tot / 1e3) / 1e9
+            row.update({"GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)})
+        kernels[name] = row
+
+    gemm_flops = sum(w.get("flops", 0) for _, _, w, _ in ops)
+    value = gemm_flops / (ms_per_step / 1e3) / 1e12
+    dom = max(per, key=lambda n: sum(per[n]["ms"]))
+    de = per[dom]
+    avg_ms = sum(de["ms"]) / len(de["ms"])
+    if de["kind"] == "gemm":
+        achieved = (de["flops"] / de["launches"]) / (avg_ms / 1e3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / FP8_PEAK_TFLOPS, 4), "traffic": None, "kernel": dom,
+                "avg_launch_us": round(1000 * avg_ms, 2)}
+    else:
+        achieved = (de["bytes"] / de["launches"]) / (avg_ms / 1e3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": dom,
+                "avg_launch_us": round(1000 * avg_ms, 2)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"timing the oracle on {args.cpu_tokens} tokens ...")
+        cpu = cpu_baseline(d, args.cpu_tokens)
+        log(f"  oracle sample took {cpu['seconds']:.1f} s")
+        cpu.pop("seconds")
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp8e4m3xfp8e4m3->fp32", "data": "synthetic",
+        "config": {"workload": "layer_sweep: 16384 tokens, seed 0, weights qkv 4096x2048, o 2048x2048, "
+                               "gate_up 12288x2048, down 2048x6144; fwd+dgrad+wgrad + 5 quantizations each",
+                   "tokens": 16384, "gemm_gflop_per_step": round(gemm_flops / 1e9, 1),
+                   "parallelism": "single GPU"},
+        "roofline": roof, "cpu_baseline": cpu, "kernels": kernels,
+    }
+    print(json.dumps(out), flush=True)
+    del keep
+
+
+if __name__ == "__main__":
+    main()

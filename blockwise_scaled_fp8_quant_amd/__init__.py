@@ -1,0 +1,188 @@
+"""Python binding of libpuro_fp8 (blockwise-scaled FP8 linear layer for MI355X / gfx950).
+
+Argument marshalling only: every function takes torch tensors that already live on the
+GPU, passes their device pointers, sizes and the current HIP stream to the C ABI
+(``include/puro_fp8.h``), allocates missing outputs with torch (device memory is all
+torch is used for), and raises ``PuroError`` on a non-zero status.  Every step of the
+computation runs in the library's HIP kernels; there is no fallback of any kind, and
+importing this package fails loudly when the shared library is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+__all__ = [
+    "LIB_PATH", "lib", "PuroError", "FWD", "DGRAD", "WGRAD", "OUT_BF16", "OUT_FP32",
+    "puro_fp8_quant_act_1x128", "puro_fp8_quant_act_128x1", "puro_fp8_quant_w_128x128",
+    "puro_fp8_gemm", "puro_fp8_gemm_workspace_size", "puro_fp8_cast_e4m3",
+    "puro_fp8_strerror", "puro_fp8_version", "EXPORTED_SYMBOLS",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpuro_fp8.so")
+
+FWD, DGRAD, WGRAD = 0, 1, 2
+OUT_BF16, OUT_FP32 = 0, 1
+MODE_NAMES = {"FWD": FWD, "DGRAD": DGRAD, "WGRAD": WGRAD}
+
+EXPORTED_SYMBOLS = (
+    "puro_fp8_quant_act_1x128", "puro_fp8_quant_act_128x1", "puro_fp8_quant_w_128x128",
+    "puro_fp8_gemm", "puro_fp8_gemm_workspace_size", "puro_fp8_cast_e4m3",
+    "puro_fp8_strerror", "puro_fp8_version",
+)
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it first (python -m blockwise_scaled_fp8_quant_amd.build "
+        f"or __graft_entry__.build()); there is no non-HIP implementation")
+
+# torch ships its own HIP runtime (same SONAME, libamdhip64.so.7).  It must be loaded
+# before the library so that the library's NEEDED entry binds to it: device pointers and
+# streams from torch are only valid in torch's runtime instance.
+import torch as _torch_runtime  # noqa: E402,F401
+
+lib = ctypes.CDLL(LIB_PATH)
+
+
+def _hip_runtimes_mapped():
+    try:
+        with open("/proc/self/maps") as f:
+            paths = {ln.split()[-1] for ln in f if "libamdhip64" in ln}
+        return {os.path.realpath(p) for p in paths}
+    except OSError:
+        return set()
+
+
+if len(_hip_runtimes_mapped()) > 1:
+    raise ImportError(f"two HIP runtimes are mapped in this process ({sorted(_hip_runtimes_mapped())}); "
+                      "import torch before any other HIP library")
+
+_i64, _p, _int, _sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+lib.puro_fp8_quant_act_1x128.argtypes = [_p, _i64, _i64, _i64, _p, _i64, _p, _p]
+lib.puro_fp8_quant_act_128x1.argtypes = [_p, _i64, _i64, _i64, _p, _i64, _p, _p]
+lib.puro_fp8_quant_w_128x128.argtypes = [_p, _i64, _i64, _i64, _p, _i64, _p, _p, _i64, _p, _p]
+lib.puro_fp8_gemm.argtypes = [_int, _i64, _i64, _i64, _p, _i64, _p, _p, _i64, _p, _p, _i64, _int, _p, _sz, _p]
+lib.puro_fp8_gemm_workspace_size.argtypes = [_int, _i64, _i64, _i64]
+lib.puro_fp8_gemm_workspace_size.restype = _sz
+lib.puro_fp8_cast_e4m3.argtypes = [_p, _i64, _p, _p]
+lib.puro_fp8_strerror.argtypes = [_int]
+lib.puro_fp8_strerror.restype = ctypes.c_char_p
+lib.puro_fp8_version.argtypes = []
+for _f in ("puro_fp8_quant_act_1x128", "puro_fp8_quant_act_128x1", "puro_fp8_quant_w_128x128",
+           "puro_fp8_gemm", "puro_fp8_cast_e4m3", "puro_fp8_version"):
+    getattr(lib, _f).restype = _int
+
+
+class PuroError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {lib.puro_fp8_strerror(status).decode()} (status {status})")
+
+
+def puro_fp8_strerror(status: int) -> str:
+    return lib.puro_fp8_strerror(status).decode()
+
+
+def puro_fp8_version() -> int:
+    return lib.puro_fp8_version()
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    return _torch().cuda.current_stream().cuda_stream
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise PuroError(status, where)
+
+
+def _ld(t) -> int:
+    return t.stride(0) if t.dim() == 2 else t.shape[-1]
+
+
+def puro_fp8_quant_act_1x128(x, q=None, s=None, stream=None) -> Tuple[object, object]:
+    """x bf16 [M, K] -> (q uint8 [M, K], s fp32 [K/128, M])."""
+    torch = _torch()
+    M, K = x.shape
+    if q is None:
+        q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    if s is None:
+        s = torch.empty((K // 128, M), dtype=torch.float32, device=x.device)
+    _check(lib.puro_fp8_quant_act_1x128(_ptr(x), M, K, _ld(x), _ptr(q), _ld(q), _ptr(s), _stream(stream)),
+           "puro_fp8_quant_act_1x128")
+    return q, s
+
+
+def puro_fp8_quant_act_128x1(x, qT=None, sT=None, stream=None) -> Tuple[object, object]:
+    """x bf16 [T, C] -> (qT uint8 [C, T], sT fp32 [T/128, C])."""
+    torch = _torch()
+    T, C = x.shape
+    if qT is None:
+        qT = torch.empty((C, T), dtype=torch.uint8, device=x.device)
+    if sT is None:
+        sT = torch.empty((T // 128, C), dtype=torch.float32, device=x.device)
+    _check(lib.puro_fp8_quant_act_128x1(_ptr(x), T, C, _ld(x), _ptr(qT), _ld(qT), _ptr(sT), _stream(stream)),
+           "puro_fp8_quant_act_128x1")
+    return qT, sT
+
+
+def puro_fp8_quant_w_128x128(w, q=None, s=None, qT=None, sT=None, transposed: bool = True, stream=None):
+    """w bf16 [N, K] -> (q [N, K], s [N/128, K/128], qT [K, N] or None, sT [K/128, N/128] or None)."""
+    torch = _torch()
+    N, K = w.shape
+    if q is None:
+        q = torch.empty((N, K), dtype=torch.uint8, device=w.device)
+    if s is None:
+        s = torch.empty((N // 128, K // 128), dtype=torch.float32, device=w.device)
+    if transposed:
+        if qT is None:
+            qT = torch.empty((K, N), dtype=torch.uint8, device=w.device)
+        if sT is None:
+            sT = torch.empty((K // 128, N // 128), dtype=torch.float32, device=w.device)
+    ldqT = _ld(qT) if qT is not None else 0
+    _check(lib.puro_fp8_quant_w_128x128(_ptr(w), N, K, _ld(w), _ptr(q), _ld(q), _ptr(s), _ptr(qT), ldqT,
+                                        _ptr(sT), _stream(stream)), "puro_fp8_quant_w_128x128")
+    return q, s, qT, sT
+
+
+def puro_fp8_gemm_workspace_size(mode: int, M: int, N: int, K: int) -> int:
+    return lib.puro_fp8_gemm_workspace_size(mode, M, N, K)
+
+
+def puro_fp8_gemm(mode, A, sA, B, sB, C=None, out_dtype: int = OUT_BF16, workspace=None, stream=None):
+    """C [M, N] = blockwise-scaled FP8 product of A [M, K] and B [N, K] (see puro_fp8.h)."""
+    torch = _torch()
+    if isinstance(mode, str):
+        mode = MODE_NAMES[mode]
+    M, K = A.shape
+    N = B.shape[0]
+    if C is None:
+        C = torch.empty((M, N), dtype=torch.bfloat16 if out_dtype == OUT_BF16 else torch.float32, device=A.device)
+    need = lib.puro_fp8_gemm_workspace_size(mode, M, N, K)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=A.device)
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.puro_fp8_gemm(mode, M, N, K, _ptr(A), _ld(A), _ptr(sA), _ptr(B), _ld(B), _ptr(sB), _ptr(C), _ld(C),
+                             out_dtype, _ptr(workspace), wbytes, _stream(stream)), "puro_fp8_gemm")
+    return C
+
+
+def puro_fp8_cast_e4m3(v, q=None, stream=None):
+    """v fp32 (any shape, contiguous) -> q uint8 codes of the same shape."""
+    torch = _torch()
+    if q is None:
+        q = torch.empty(v.shape, dtype=torch.uint8, device=v.device)
+    _check(lib.puro_fp8_cast_e4m3(_ptr(v), v.numel(), _ptr(q), _stream(stream)), "puro_fp8_cast_e4m3")
+    return q

@@ -1,0 +1,119 @@
+// C-ABI layer: argument validation on the host, then one asynchronous launch on the
+// caller's stream.  Every check runs before any HIP call; a failed check launches nothing.
+#include "../../include/puro_fp8.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include "internal.hpp"
+
+namespace {
+
+constexpr int64_t kGroup = 128;
+constexpr int64_t kIntMax = 0x7FFFFFFF;
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline int from_hip(hipError_t e) {
+  if (e == hipErrorInvalidConfiguration) return PURO_ERR_UNSUPPORTED;
+  return e == hipSuccess ? PURO_OK : PURO_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int puro_fp8_quant_act_1x128(const void* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q, int64_t ldq,
+                             float* s, hipStream_t st) {
+  if (M < 0 || K < 0) return PURO_ERR_SHAPE;
+  if (K % kGroup) return PURO_ERR_SHAPE;
+  if (M == 0 || K == 0) return PURO_OK;
+  if (!x || !q || !s) return PURO_ERR_NULLPTR;
+  if (!aligned16(x) || !aligned16(q) || !aligned16(s)) return PURO_ERR_ALIGN;
+  if (ldx < K || ldq < K || (ldx * 2) % 16 || ldq % 16) return PURO_ERR_LD;
+  if (K / kGroup > kIntMax) return PURO_ERR_UNSUPPORTED;
+  return from_hip(puro::launch_quant_1x128(x, M, K, ldx, q, ldq, s, st));
+}
+
+int puro_fp8_quant_act_128x1(const void* x, int64_t T, int64_t C, int64_t ldx, uint8_t* qT, int64_t ldqT,
+                             float* sT, hipStream_t st) {
+  if (T < 0 || C < 0) return PURO_ERR_SHAPE;
+  if (T % kGroup || C % 8) return PURO_ERR_SHAPE;
+  if (T == 0 || C == 0) return PURO_OK;
+  if (!x || !qT || !sT) return PURO_ERR_NULLPTR;
+  if (!aligned16(x) || !aligned16(qT) || !aligned16(sT)) return PURO_ERR_ALIGN;
+  if (ldx < C || ldqT < T || (ldx * 2) % 16 || ldqT % 16) return PURO_ERR_LD;
+  if (T / kGroup > 65535) return PURO_ERR_UNSUPPORTED;
+  return from_hip(puro::launch_quant_128x1(x, T, C, ldx, qT, ldqT, sT, st));
+}
+
+int puro_fp8_quant_w_128x128(const void* w, int64_t N, int64_t K, int64_t ldw, uint8_t* q, int64_t ldq,
+                             float* s, uint8_t* qT, int64_t ldqT, float* sT, hipStream_t st) {
+  if (N < 0 || K < 0) return PURO_ERR_SHAPE;
+  if (N % kGroup || K % kGroup) return PURO_ERR_SHAPE;
+  if ((qT == nullptr) != (sT == nullptr)) return PURO_ERR_NULLPTR;
+  if (N == 0 || K == 0) return PURO_OK;
+  if (!w || !q || !s) return PURO_ERR_NULLPTR;
+  if (!aligned16(w) || !aligned16(q) || !aligned16(s)) return PURO_ERR_ALIGN;
+  if (qT && (!aligned16(qT) || !aligned16(sT))) return PURO_ERR_ALIGN;
+  if (ldw < K || ldq < K || (ldw * 2) % 16 || ldq % 16) return PURO_ERR_LD;
+  if (qT && (ldqT < N || ldqT % 16)) return PURO_ERR_LD;
+  if (N / kGroup > 65535) return PURO_ERR_UNSUPPORTED;
+  return from_hip(puro::launch_quant_128x128(w, N, K, ldw, q, ldq, s, qT, ldqT, sT, st));
+}
+
+int puro_fp8_gemm(int mode, int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda, const float* sA,
+                  const uint8_t* B, int64_t ldb, const float* sB, void* C, int64_t ldc, int out_dtype,
+                  void* workspace, size_t workspace_bytes, hipStream_t st) {
+  if (mode != PURO_GEMM_FWD && mode != PURO_GEMM_DGRAD && mode != PURO_GEMM_WGRAD) return PURO_ERR_MODE;
+  if (out_dtype != PURO_OUT_BF16 && out_dtype != PURO_OUT_FP32) return PURO_ERR_DTYPE;
+  if (M < 0 || N < 0 || K < 0) return PURO_ERR_SHAPE;
+  if (M % kGroup || N % kGroup || K % kGroup) return PURO_ERR_SHAPE;
+  if (M == 0 || N == 0) return PURO_OK;
+  const int64_t es = out_dtype == PURO_OUT_BF16 ? 2 : 4;
+  if (!C) return PURO_ERR_NULLPTR;
+  if (!aligned16(C)) return PURO_ERR_ALIGN;
+  if (ldc < N || (ldc * es) % 16) return PURO_ERR_LD;
+  if (K > 0) {
+    if (!A || !B || !sA || !sB) return PURO_ERR_NULLPTR;
+    if (!aligned16(A) || !aligned16(B) || !aligned16(sA) || !aligned16(sB)) return PURO_ERR_ALIGN;
+    if (lda < K || ldb < K || lda % 16 || ldb % 16) return PURO_ERR_LD;
+  }
+  if (M > kIntMax || N > kIntMax || K > kIntMax) return PURO_ERR_UNSUPPORTED;
+  const size_t need = puro::gemm_workspace_bytes(mode, M, N, K);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return PURO_ERR_WORKSPACE;
+  return from_hip(puro::launch_gemm(mode, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, out_dtype == PURO_OUT_BF16,
+                                    workspace, workspace_bytes, st));
+}
+
+size_t puro_fp8_gemm_workspace_size(int mode, int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || K <= 0) return 0;
+  return puro::gemm_workspace_bytes(mode, M, N, K);
+}
+
+int puro_fp8_cast_e4m3(const float* v, int64_t n, uint8_t* q, hipStream_t st) {
+  if (n < 0) return PURO_ERR_SHAPE;
+  if (n == 0) return PURO_OK;
+  if (!v || !q) return PURO_ERR_NULLPTR;
+  if (!aligned16(v) || !aligned16(q)) return PURO_ERR_ALIGN;
+  return from_hip(puro::launch_cast_e4m3(v, n, q, st));
+}
+
+const char* puro_fp8_strerror(int status) {
+  switch (status) {
+    case PURO_OK: return "ok";
+    case PURO_ERR_NULLPTR: return "null pointer (or only one of an optional pointer pair)";
+    case PURO_ERR_SHAPE: return "bad shape (negative, or not a multiple of 128 where required)";
+    case PURO_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case PURO_ERR_LD: return "bad leading dimension (smaller than the row, or not a multiple of 16 bytes)";
+    case PURO_ERR_MODE: return "unknown GEMM mode";
+    case PURO_ERR_DTYPE: return "unknown output dtype";
+    case PURO_ERR_WORKSPACE: return "workspace too small";
+    case PURO_ERR_HIP: return "HIP runtime error at launch";
+    case PURO_ERR_UNSUPPORTED: return "request outside what this build implements";
+    default: return "unknown status";
+  }
+}
+
+int puro_fp8_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,27 @@
+// Internal launcher declarations between the C-ABI layer (abi.cpp) and the kernels.
+// Shapes and pointers are validated by the caller before any of these runs.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace puro {
+
+hipError_t launch_quant_1x128(const void* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
+                              int64_t ldq, float* s, hipStream_t st);
+hipError_t launch_quant_128x1(const void* x, int64_t T, int64_t C, int64_t ldx, uint8_t* qT,
+                              int64_t ldqT, float* sT, hipStream_t st);
+hipError_t launch_quant_128x128(const void* w, int64_t N, int64_t K, int64_t ldw, uint8_t* q,
+                                int64_t ldq, float* s, uint8_t* qT, int64_t ldqT, float* sT,
+                                hipStream_t st);
+hipError_t launch_cast_e4m3(const float* v, int64_t n, uint8_t* q, hipStream_t st);
+
+// GEMM: mode 0 FWD, 1 DGRAD, 2 WGRAD; out_bf16 selects bf16 (else fp32) output.
+size_t gemm_workspace_bytes(int mode, int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm(int mode, int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
+                       const float* sA, const uint8_t* B, int64_t ldb, const float* sB, void* C,
+                       int64_t ldc, bool out_bf16, void* workspace, size_t workspace_bytes,
+                       hipStream_t st);
+
+}  // namespace puro

@@ -1,0 +1,284 @@
+// gfx950 quantizer kernels: 1x128 activation groups, 128x1 token groups written
+// transposed (wgrad operands), 128x128 weight blocks (+ optional transposed copy), and
+// the standalone fp32 -> E4M3 cast used to verify the device codec.
+//
+// All three quantizers are HBM-bound streams (2 B read + 1 B written per element plus
+// one 4-byte scale per tile); the kernels use 16-byte coalesced loads and stores, keep
+// the tile in registers, reduce amax with DPP / cross-lane moves (and LDS across waves
+// where a tile spans waves), and run the per-element work as one fp32 multiply and half
+// a packed FP8 convert.
+#include "codec.hpp"
+#include "internal.hpp"
+
+
+namespace puro {
+
+// ---------------------------------------------------------------------------------------
+// 1x128: one wave covers 4 rows x 1 group per step (16 lanes x 16 B = one 128-element
+// group); each wave handles U consecutive groups of its 4 rows, so every lane keeps U
+// 16-byte loads in flight.  A workgroup is 4 waves = 16 rows.  Scales of the 4 rows of a
+// group are adjacent in the kb-major scale array, so one store instruction writes them.
+// ---------------------------------------------------------------------------------------
+template <int U>
+__global__ __launch_bounds__(256) void quant_1x128_kernel(const uint16_t* __restrict__ x, int64_t M,
+                                                          int G, int64_t ldx, uint8_t* __restrict__ q,
+                                                          int64_t ldq, float* __restrict__ s,
+                                                          int nkbb) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int ro = lane >> 4;
+  const int c = lane & 15;
+  const int64_t rb = blockIdx.x / nkbb;
+  const int kb0 = (blockIdx.x - (int)(rb * nkbb)) * U;
+  const int64_t row = rb * 16 + wave * 4 + ro;
+  const bool row_ok = row < M;
+
+  u32x4 v[U];
+  const uint16_t* xr = x + row * ldx + c * 8;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int kb = kb0 + u;
+    if (row_ok && kb < G)
+      v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xr + kb * 128));
+    else
+      v[u] = u32x4{0u, 0u, 0u, 0u};
+  }
+  uint8_t* qr = q + row * ldq + c * 8;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int kb = kb0 + u;
+    uint32_t m = pk_max_u16(pk_max_u16(abs2(v[u].x), abs2(v[u].y)), pk_max_u16(abs2(v[u].z), abs2(v[u].w)));
+    m = row16_max(hmax16(m));
+    float sc, r;
+    tile_scale(m, sc, r);
+    u32x2 o;
+    o.x = cvt4(bf16_lo(v[u].x) * r, bf16_hi(v[u].x) * r, bf16_lo(v[u].y) * r, bf16_hi(v[u].y) * r);
+    o.y = cvt4(bf16_lo(v[u].z) * r, bf16_hi(v[u].z) * r, bf16_lo(v[u].w) * r, bf16_hi(v[u].w) * r);
+    if (row_ok && kb < G) {
+      __builtin_nontemporal_store(o, reinterpret_cast<u32x2*>(qr + kb * 128));
+      if (c == 0) s[(int64_t)kb * M + row] = sc;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// 128x1, transposed output.  A workgroup owns 128 tokens x 64 columns.  Thread t holds
+// 4 consecutive tokens (4*(t>>3) .. +3) x 8 consecutive columns (8*(t&7) .. +7), loaded
+// as four coalesced 16-byte reads (8 lanes read one 128-byte row segment).  Column amax:
+// packed 16-bit max over the thread's 4 tokens, then across the 8 lanes of the wave
+// sharing a column chunk, then across the 4 waves in LDS.  Because a thread holds 4
+// consecutive tokens of each of its columns, one packed convert pair yields the 4 output
+// bytes of a column directly; the dwords are staged through LDS ([column][token quad],
+// odd row stride against bank conflicts) so every output row of 128 bytes is written by
+// 8 lanes with 16-byte stores.
+// ---------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void quant_128x1_kernel(const uint16_t* __restrict__ x, int64_t T,
+                                                          int64_t C, int64_t ldx,
+                                                          uint8_t* __restrict__ qT, int64_t ldqT,
+                                                          float* __restrict__ sT) {
+  __shared__ uint32_t red[4][32];
+  __shared__ float rsh[64];
+  __shared__ uint32_t stage[64 * 33];
+
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  const int cc = t & 7;
+  const int rq = t >> 3;
+  const int64_t tb = blockIdx.y;
+  const int64_t c0 = (int64_t)blockIdx.x * 64;
+  const int64_t col = c0 + cc * 8;
+  const bool ok = col < C;
+
+  u32x4 v[4];
+  const uint16_t* xp = x + (tb * 128 + rq * 4) * ldx + col;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    v[j] = ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xp + j * ldx))
+              : u32x4{0u, 0u, 0u, 0u};
+
+  uint32_t m[4];
+  m[0] = pk_max_u16(pk_max_u16(abs2(v[0].x), abs2(v[1].x)), pk_max_u16(abs2(v[2].x), abs2(v[3].x)));
+  m[1] = pk_max_u16(pk_max_u16(abs2(v[0].y), abs2(v[1].y)), pk_max_u16(abs2(v[2].y), abs2(v[3].y)));
+  m[2] = pk_max_u16(pk_max_u16(abs2(v[0].z), abs2(v[1].z)), pk_max_u16(abs2(v[2].z), abs2(v[3].z)));
+  m[3] = pk_max_u16(pk_max_u16(abs2(v[0].w), abs2(v[1].w)), pk_max_u16(abs2(v[2].w), abs2(v[3].w)));
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    m[d] = pk_max_u16(m[d], (uint32_t)__shfl_xor((int)m[d], 8));
+    m[d] = pk_max_u16(m[d], (uint32_t)__shfl_xor((int)m[d], 16));
+    m[d] = pk_max_u16(m[d], (uint32_t)__shfl_xor((int)m[d], 32));
+  }
+  if (lane < 8) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) red[wave][cc * 4 + d] = m[d];
+  }
+  __syncthreads();
+  if (t < 64) {
+    const int idx = (t >> 3) * 4 + ((t & 7) >> 1);
+    uint32_t w = pk_max_u16(pk_max_u16(red[0][idx], red[1][idx]), pk_max_u16(red[2][idx], red[3][idx]));
+    const uint32_t a = (t & 1) ? (w >> 16) : (w & 0xFFFFu);
+    float sc, r;
+    tile_scale(a, sc, r);
+    rsh[t] = r;
+    if (c0 + t < C) sT[tb * C + c0 + t] = sc;
+  }
+  __syncthreads();
+
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float r = rsh[cc * 8 + i];
+    float e[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t w = v[j][i >> 1];
+      e[j] = ((i & 1) ? bf16_hi(w) : bf16_lo(w)) * r;
+    }
+    stage[(cc * 8 + i) * 33 + rq] = cvt4(e[0], e[1], e[2], e[3]);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int cl = (t >> 3) + 32 * it;
+    const int part = t & 7;
+    const uint32_t* sp = stage + cl * 33 + part * 4;
+    const u32x4 o = {sp[0], sp[1], sp[2], sp[3]};
+    if (c0 + cl < C)
+      __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(qT + (c0 + cl) * ldqT + tb * 128 + part * 16));
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// 128x128 weight blocks.  One workgroup per block; thread t holds rows 8*(t>>4) .. +7 of
+// the block at columns 8*(t&15) .. +7 (8 coalesced 16-byte loads).  Block amax: packed
+// max in registers, DPP/cross-lane max in the wave, LDS across the 4 waves.  The thread's
+// 8x8 sub-block is converted twice: row-wise for q and column-wise for the transposed
+// copy qT (8 consecutive rows of one column form the 8 bytes of a qT row segment).
+// ---------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void quant_128x128_kernel(const uint16_t* __restrict__ w, int64_t N,
+                                                            int64_t K, int64_t ldw,
+                                                            uint8_t* __restrict__ q, int64_t ldq,
+                                                            float* __restrict__ s,
+                                                            uint8_t* __restrict__ qT, int64_t ldqT,
+                                                            float* __restrict__ sT) {
+  __shared__ uint32_t red[4];
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  const int cc = t & 15;
+  const int rg = t >> 4;
+  const int64_t kb = blockIdx.x, nb = blockIdx.y;
+  const int64_t n0 = nb * 128 + rg * 8;
+  const int64_t k0 = kb * 128 + cc * 8;
+
+  u32x4 v[8];
+  const uint16_t* wp = w + n0 * ldw + k0;
+#pragma unroll
+  for (int p = 0; p < 8; ++p)
+    v[p] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wp + p * ldw));
+
+  uint32_t m = 0;
+#pragma unroll
+  for (int p = 0; p < 8; ++p)
+    m = pk_max_u16(m, pk_max_u16(pk_max_u16(abs2(v[p].x), abs2(v[p].y)), pk_max_u16(abs2(v[p].z), abs2(v[p].w))));
+  m = wave_max(hmax16(m));
+  if (lane == 0) red[wave] = m;
+  __syncthreads();
+  m = umax(umax(red[0], red[1]), umax(red[2], red[3]));
+  float sc, r;
+  tile_scale(m, sc, r);
+  if (t == 0) {
+    const int64_t KB = K >> 7, NB = N >> 7;
+    s[nb * KB + kb] = sc;
+    if (sT) sT[kb * NB + nb] = sc;
+  }
+
+  float f[8][8];
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    f[p][0] = bf16_lo(v[p].x) * r; f[p][1] = bf16_hi(v[p].x) * r;
+    f[p][2] = bf16_lo(v[p].y) * r; f[p][3] = bf16_hi(v[p].y) * r;
+    f[p][4] = bf16_lo(v[p].z) * r; f[p][5] = bf16_hi(v[p].z) * r;
+    f[p][6] = bf16_lo(v[p].w) * r; f[p][7] = bf16_hi(v[p].w) * r;
+  }
+  uint8_t* qp = q + n0 * ldq + k0;
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    u32x2 o;
+    o.x = cvt4(f[p][0], f[p][1], f[p][2], f[p][3]);
+    o.y = cvt4(f[p][4], f[p][5], f[p][6], f[p][7]);
+    __builtin_nontemporal_store(o, reinterpret_cast<u32x2*>(qp + p * ldq));
+  }
+  if (qT) {
+    uint8_t* tp = qT + k0 * ldqT + n0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      u32x2 o;
+      o.x = cvt4(f[0][i], f[1][i], f[2][i], f[3][i]);
+      o.y = cvt4(f[4][i], f[5][i], f[6][i], f[7][i]);
+      __builtin_nontemporal_store(o, reinterpret_cast<u32x2*>(tp + i * ldqT));
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Standalone saturating cast: 4 floats -> one dword of codes per step.
+// ---------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void cast_e4m3_kernel(const float* __restrict__ v, int64_t n,
+                                                        uint8_t* __restrict__ q) {
+  const int64_t n4 = n >> 2;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
+    const float4 f = reinterpret_cast<const float4*>(v)[i];
+    reinterpret_cast<uint32_t*>(q)[i] = cvt4(sat448(f.x), sat448(f.y), sat448(f.z), sat448(f.w));
+  }
+  const int64_t tail = n & 3;
+  if (tail && blockIdx.x == 0 && threadIdx.x < tail) {
+    const int64_t i = n4 * 4 + threadIdx.x;
+    q[i] = (uint8_t)(cvt2_lo(sat448(v[i]), 0.0f, 0u) & 0xFFu);
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Host-side launchers (shapes already validated by the ABI layer).
+// ---------------------------------------------------------------------------------------
+hipError_t launch_quant_1x128(const void* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
+                              int64_t ldq, float* s, hipStream_t st) {
+  constexpr int U = 4;
+  const int G = (int)(K / 128);
+  const int nkbb = (G + U - 1) / U;
+  const int64_t nrb = (M + 15) / 16;
+  const int64_t blocks = nrb * nkbb;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(quant_1x128_kernel<U>, dim3((unsigned)blocks), dim3(256), 0, st,
+                     static_cast<const uint16_t*>(x), M, G, ldx, q, ldq, s, nkbb);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_128x1(const void* x, int64_t T, int64_t C, int64_t ldx, uint8_t* qT,
+                              int64_t ldqT, float* sT, hipStream_t st) {
+  const int64_t gx = (C + 63) / 64, gy = T / 128;
+  if (gx > 0x7FFFFFFF || gy > 65535) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(quant_128x1_kernel, dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, st,
+                     static_cast<const uint16_t*>(x), T, C, ldx, qT, ldqT, sT);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_128x128(const void* w, int64_t N, int64_t K, int64_t ldw, uint8_t* q,
+                                int64_t ldq, float* s, uint8_t* qT, int64_t ldqT, float* sT,
+                                hipStream_t st) {
+  const int64_t gx = K / 128, gy = N / 128;
+  if (gx > 0x7FFFFFFF || gy > 65535) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(quant_128x128_kernel, dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, st,
+                     static_cast<const uint16_t*>(w), N, K, ldw, q, ldq, s, qT, ldqT, sT);
+  return hipGetLastError();
+}
+
+hipError_t launch_cast_e4m3(const float* v, int64_t n, uint8_t* q, hipStream_t st) {
+  int64_t blocks = ((n >> 2) + 255) / 256;
+  if (blocks < 1) blocks = 1;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(cast_e4m3_kernel, dim3((unsigned)blocks), dim3(256), 0, st, v, n, q);
+  return hipGetLastError();
+}
+
+}  // namespace puro

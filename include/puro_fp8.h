@@ -1,0 +1,148 @@
+/*
+ * puro_fp8.h -- C ABI of the blockwise-scaled FP8 linear-layer library (MI355X / gfx950).
+ *
+ * The method: the main linear layers of a Transformer run their matmuls in FP8 with
+ * fine-grained block scaling after DeepSeek-V3, while numerically sensitive work and
+ * master weights / optimizer state stay in BF16 / FP32 (ModelScope write-up
+ * "清华开源 Puro-2B：4400 美元训练，15 项任务平均指标超 Qwen2-1.5B！", section
+ * 精度: FP8 分块量化与净效率收益).  Activations are grouped by 128 and weights use
+ * 128x128 blocks (agihunt digest "清华用消费级 5090 花 6890 美元从零训 2B，15 项均分超过
+ * Qwen2", section 方法 / Method, FP8 bullet); each block carries its own scale so that
+ * one outlier does not inflate a scale shared by the whole tensor (same digest,
+ * section 术语 / glossary, "blockwise FP8").
+ *
+ * Numerics fixed by this library where the pages are silent:
+ *   - FP8 format: OCP E4M3 (bias 7, largest finite 448, NaN = S.1111.111, no inf).
+ *   - Per tile: amax = max|x| (exact, from the bf16 input); amax_eff = max(amax, 2^-96);
+ *     scale s = fl32(amax_eff / 448) (stored); r = fl32(448 / amax_eff);
+ *     code = E4M3(fl32(x * r)) with round-to-nearest-even, saturating at 448, sign kept.
+ *     Both divisions are correctly rounded fp32 divisions.
+ *   - GEMM: for every 128-deep contraction slice kb, the FP8 products are accumulated in
+ *     fp32 (matrix cores) and then added, multiplied by sA(i,kb) * sB(j,kb), into a
+ *     separate fp32 accumulator; the result is written as bf16 (round to nearest even)
+ *     or fp32.  Exact result: C[i,j] = sum_k dec(A[i,k]) sA(i,k/128) dec(B[j,k]) sB(j,k/128).
+ *   - Non-finite input is outside the bit-exact contract: a NaN in a tile makes its scale
+ *     and codes NaN; an infinity gives that tile's scale +inf.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers (HIP device memory); the caller owns every
+ *     buffer; the library allocates nothing and keeps no per-call state.
+ *   - Matrices are row-major; a leading dimension ("ld") is the distance, in ELEMENTS of
+ *     that buffer's type, between consecutive rows; ld >= row width.
+ *   - Pointers must be 16-byte aligned and ld * element_size must be a multiple of 16.
+ *   - Work is enqueued asynchronously on the caller's stream `st` (NULL = the null stream);
+ *     nothing synchronizes.  Device faults surface at the caller's next synchronization.
+ *   - Every argument check runs on the host before any HIP call; a failed check returns a
+ *     negative status and launches nothing.  A dimension of 0 is a no-op returning
+ *     PURO_OK.  After a launch, a HIP launch error is reported as PURO_ERR_HIP.
+ *   - Thread-safe: concurrent calls on different streams are independent.
+ */
+#ifndef PURO_FP8_H
+#define PURO_FP8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* hipStream_t;
+
+enum {
+  PURO_OK = 0,
+  PURO_ERR_NULLPTR = -1,     /* a required pointer is NULL, or exactly one of an optional pair */
+  PURO_ERR_SHAPE = -2,       /* a dimension is negative or not a multiple of 128 where required */
+  PURO_ERR_ALIGN = -3,       /* a pointer is not 16-byte aligned */
+  PURO_ERR_LD = -4,          /* ld < width, or ld * element size not a multiple of 16 bytes */
+  PURO_ERR_MODE = -5,        /* unknown GEMM mode */
+  PURO_ERR_DTYPE = -6,       /* unknown output dtype */
+  PURO_ERR_WORKSPACE = -7,   /* workspace smaller than puro_fp8_gemm_workspace_size() */
+  PURO_ERR_HIP = -8,         /* the HIP runtime reported an error at launch */
+  PURO_ERR_UNSUPPORTED = -9  /* valid request this build does not implement (e.g. a size limit) */
+};
+
+enum { PURO_GEMM_FWD = 0, PURO_GEMM_DGRAD = 1, PURO_GEMM_WGRAD = 2 };
+enum { PURO_OUT_BF16 = 0, PURO_OUT_FP32 = 1 };
+
+/*
+ * 1x128 activation quantizer (forward X, dgrad dY).  Groups of 128 consecutive features
+ * of one row share a scale (agihunt digest, section 方法, FP8 bullet: activations grouped
+ * by 128; the group runs along the GEMM's contraction axis).
+ *   x   : bf16 [M, K], row stride ldx (elements); K % 128 == 0; M >= 0 arbitrary.
+ *   q   : uint8 E4M3 codes [M, K], row stride ldq (bytes).
+ *   s   : fp32 scales, contraction-block-major [K/128][M] (contiguous, stride M): s[kb*M + m]
+ *         is the scale of row m, columns 128kb .. 128kb+127.
+ */
+int puro_fp8_quant_act_1x128(const void* x, int64_t M, int64_t K, int64_t ldx,
+                             uint8_t* q, int64_t ldq, float* s, hipStream_t st);
+
+/*
+ * 128x1 activation / gradient quantizer for the wgrad operands, written transposed.
+ * Groups of 128 consecutive tokens of one column share a scale (the wgrad contraction
+ * runs over tokens; same passages as above).
+ *   x   : bf16 [T, C], row stride ldx (elements); T % 128 == 0; C % 8 == 0.
+ *   qT  : uint8 codes [C, T] (token-contiguous), row stride ldqT (bytes).
+ *   sT  : fp32 scales [T/128][C] (contiguous, stride C): sT[tb*C + c] is the scale of
+ *         column c, tokens 128tb .. 128tb+127.
+ */
+int puro_fp8_quant_act_128x1(const void* x, int64_t T, int64_t C, int64_t ldx,
+                             uint8_t* qT, int64_t ldqT, float* sT, hipStream_t st);
+
+/*
+ * 128x128 weight-block quantizer (agihunt digest, section 方法, FP8 bullet: weights in
+ * 128x128 blocks), with an optional transposed copy for dgrad.
+ *   w   : bf16 [N, K], row stride ldw (elements); N % 128 == 0, K % 128 == 0.
+ *   q   : uint8 codes [N, K], row stride ldq (bytes).
+ *   s   : fp32 scales [N/128][K/128] row-major.
+ *   qT  : optional uint8 codes [K, N], row stride ldqT: qT[k][n] == q[n][k].
+ *   sT  : optional fp32 scales [K/128][N/128]: sT[kb][nb] == s[nb][kb].
+ *   qT and sT are both NULL or both non-NULL (else PURO_ERR_NULLPTR).
+ */
+int puro_fp8_quant_w_128x128(const void* w, int64_t N, int64_t K, int64_t ldw,
+                             uint8_t* q, int64_t ldq, float* s,
+                             uint8_t* qT, int64_t ldqT, float* sT, hipStream_t st);
+
+/*
+ * Blockwise-scaled FP8 GEMM  C[M,N] = sum_kb sA(i,kb) sB(j,kb) sum_{k in kb} dec(A[i,k]) dec(B[j,k]).
+ * ModelScope write-up, section 精度 (FP8 matmuls of the main linear layers, DeepSeek-V3
+ * block scaling); per-slice fp32 promotion into a separate fp32 accumulator.
+ *   mode: PURO_GEMM_FWD   Y  = X  W^T : A = Xq   [T, Din],  B = Wq  [Dout, Din]
+ *         PURO_GEMM_DGRAD dX = dY W   : A = dYq  [T, Dout], B = WqT [Din, Dout]
+ *         PURO_GEMM_WGRAD dW = dY^T X : A = dYqT [Dout, T], B = XqT [Din, T]
+ *   A   : uint8 codes [M, K], row stride lda (bytes); sA: fp32 [K/128][M].
+ *   B   : uint8 codes [N, K], row stride ldb (bytes);
+ *         sB: FWD/DGRAD fp32 [N/128][K/128] (128x128 blocks); WGRAD fp32 [K/128][N].
+ *   C   : [M, N] bf16 (out_dtype PURO_OUT_BF16) or fp32 (PURO_OUT_FP32), row stride ldc
+ *         (elements).  M, N, K must be multiples of 128 (else PURO_ERR_SHAPE).
+ *   workspace / workspace_bytes: scratch the caller provides; must be at least
+ *         puro_fp8_gemm_workspace_size(mode, M, N, K) bytes (may be NULL when that is 0).
+ *   The summation order inside the GEMM is not part of the contract.
+ */
+int puro_fp8_gemm(int mode, int64_t M, int64_t N, int64_t K,
+                  const uint8_t* A, int64_t lda, const float* sA,
+                  const uint8_t* B, int64_t ldb, const float* sB,
+                  void* C, int64_t ldc, int out_dtype,
+                  void* workspace, size_t workspace_bytes, hipStream_t st);
+
+/* Bytes of workspace puro_fp8_gemm needs for this problem (0 = none). */
+size_t puro_fp8_gemm_workspace_size(int mode, int64_t M, int64_t N, int64_t K);
+
+/*
+ * Verification helper: the device fp32 -> E4M3 cast every quantizer uses
+ * (round-to-nearest-even, saturating at 448, sign kept, NaN -> NaN code), applied
+ * elementwise: q[i] = E4M3(v[i]) for 0 <= i < n.  v and q must be 16-byte aligned.
+ */
+int puro_fp8_cast_e4m3(const float* v, int64_t n, uint8_t* q, hipStream_t st);
+
+/* Human-readable text of a status code (static storage). */
+const char* puro_fp8_strerror(int status);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int puro_fp8_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PURO_FP8_H */

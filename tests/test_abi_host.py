@@ -1,0 +1,128 @@
+"""Host-side checks of the C-ABI library (no GPU needed, no kernel launched).
+
+- the shared library loads and exports every entry point include/puro_fp8.h declares;
+- version / strerror;
+- argument validation: every call below has at least one invalid argument (or an empty
+  shape), so the library returns before making any HIP call.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "puro_fp8.h")
+
+import blockwise_scaled_fp8_quant_amd as P  # noqa: E402
+
+OK, NULLPTR, SHAPE, ALIGN, LD, MODE, DTYPE, WORKSPACE, HIP, UNSUP = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9
+A16 = 0x10000          # a fake, 16-byte aligned address: never dereferenced (validation fails first)
+MIS = 0x10008          # misaligned
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(puro_fp8_\w+)\s*\(", src)))
+
+
+def test_header_and_binding_agree():
+    decl = declared_functions()
+    assert len(decl) == 8
+    assert sorted(P.EXPORTED_SYMBOLS) == decl
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(P.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = os.popen(f"nm -D --defined-only {P.LIB_PATH}").read()
+    for name in declared_functions():
+        assert re.search(rf"\bT {name}\b", out), name
+
+
+def test_version_and_strerror():
+    assert P.puro_fp8_version() >= 100
+    for st in (OK, NULLPTR, SHAPE, ALIGN, LD, MODE, DTYPE, WORKSPACE, HIP, UNSUP):
+        assert P.puro_fp8_strerror(st) and P.puro_fp8_strerror(st) != "unknown status"
+    assert P.puro_fp8_strerror(12345) == "unknown status"
+
+
+def q1(x=A16, M=256, K=512, ldx=512, q=A16, ldq=512, s=A16):
+    return P.lib.puro_fp8_quant_act_1x128(x, M, K, ldx, q, ldq, s, None)
+
+
+def test_quant_1x128_validation():
+    assert q1(M=0) == OK and q1(K=0) == OK
+    assert q1(M=-1) == SHAPE and q1(K=100) == SHAPE
+    assert q1(x=None) == NULLPTR and q1(q=None) == NULLPTR and q1(s=None) == NULLPTR
+    assert q1(x=MIS) == ALIGN and q1(q=MIS) == ALIGN and q1(s=A16 + 4) == ALIGN
+    assert q1(ldx=384) == LD and q1(ldq=500) == LD and q1(ldx=516) == LD
+
+
+def q128x1(x=A16, T=256, C=64, ldx=64, qT=A16, ldqT=256, sT=A16):
+    return P.lib.puro_fp8_quant_act_128x1(x, T, C, ldx, qT, ldqT, sT, None)
+
+
+def test_quant_128x1_validation():
+    assert q128x1(T=0) == OK and q128x1(C=0) == OK
+    assert q128x1(T=100) == SHAPE and q128x1(C=12) == SHAPE and q128x1(T=-128) == SHAPE
+    assert q128x1(x=None) == NULLPTR and q128x1(sT=None) == NULLPTR
+    assert q128x1(qT=MIS) == ALIGN
+    assert q128x1(ldx=32) == LD and q128x1(ldqT=128) == LD and q128x1(ldqT=264) == LD
+
+
+def qw(w=A16, N=256, K=256, ldw=256, q=A16, ldq=256, s=A16, qT=A16, ldqT=256, sT=A16):
+    return P.lib.puro_fp8_quant_w_128x128(w, N, K, ldw, q, ldq, s, qT, ldqT, sT, None)
+
+
+def test_quant_w_validation():
+    assert qw(N=0) == OK
+    assert qw(N=200) == SHAPE and qw(K=64) == SHAPE
+    assert qw(qT=None) == NULLPTR and qw(sT=None) == NULLPTR and qw(w=None) == NULLPTR
+    assert qw(qT=MIS) == ALIGN and qw(w=MIS) == ALIGN
+    assert qw(ldw=128) == LD and qw(ldqT=128) == LD and qw(ldq=264) == LD
+
+
+def gm(mode=0, M=256, N=256, K=256, A=A16, lda=256, sA=A16, B=A16, ldb=256, sB=A16, C=A16, ldc=256,
+       dt=0, ws=None, wsb=0):
+    return P.lib.puro_fp8_gemm(mode, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, dt, ws, wsb, None)
+
+
+def test_gemm_validation():
+    assert gm(M=0) == OK and gm(N=0) == OK
+    assert gm(mode=3) == MODE and gm(mode=-1) == MODE
+    assert gm(dt=2) == DTYPE
+    assert gm(M=200) == SHAPE and gm(K=-128) == SHAPE and gm(N=100) == SHAPE
+    assert gm(C=None) == NULLPTR and gm(A=None) == NULLPTR and gm(sB=None) == NULLPTR
+    assert gm(A=MIS) == ALIGN and gm(C=MIS) == ALIGN and gm(sA=A16 + 4) == ALIGN
+    assert gm(lda=128) == LD and gm(ldc=128) == LD and gm(ldb=264) == LD
+    assert gm(ldc=262, dt=0) == LD       # 262 * 2 bytes is not a multiple of 16
+
+
+def test_gemm_validation_fp32_ld_rule():
+    # ldc * 4 must be a multiple of 16: 260 qualifies (>= N), 258 does not
+    assert gm(ldc=258, dt=1) == LD
+
+
+def test_workspace_query():
+    for mode in (0, 1, 2):
+        assert P.puro_fp8_gemm_workspace_size(mode, 0, 128, 128) == 0
+        assert P.puro_fp8_gemm_workspace_size(mode, 4096, 4096, 2048) >= 0
+
+
+def test_cast_validation():
+    assert P.lib.puro_fp8_cast_e4m3(A16, 0, A16, None) == OK
+    assert P.lib.puro_fp8_cast_e4m3(A16, -1, A16, None) == SHAPE
+    assert P.lib.puro_fp8_cast_e4m3(None, 4, A16, None) == NULLPTR
+    assert P.lib.puro_fp8_cast_e4m3(MIS, 4, A16, None) == ALIGN
+
+
+def test_product_path_never_imports_oracle():
+    pkg = os.path.join(ROOT, "blockwise_scaled_fp8_quant_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".hpp", ".h")):
+                src = open(os.path.join(dirpath, f)).read()
+                assert "from oracle" not in src and "import oracle" not in src, f
