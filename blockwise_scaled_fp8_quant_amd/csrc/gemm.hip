@@ -5,13 +5,31 @@
 // P_kb is produced by the FP8 matrix cores (v_mfma_f32_32x32x64_f8f6f4, E4M3 x E4M3 ->
 // fp32; two instructions cover one 128-deep slice of a 32x32 output tile), and the
 // promotion C_acc += P_kb * (sA * sB) runs on the vector ALUs into a separate fp32
-// accumulator, as the DeepSeek-V3-style fine-grained scheme the pages follow prescribes
+// accumulator, following the DeepSeek-V3-style fine-grained scheme the pages adopt
 // (ModelScope write-up on Puro-2B, section 精度).
 //
-// Operand roles inside the MFMA are swapped (the B tile is the instruction's A operand)
-// so that every lane owns ONE output row i and 16 output columns: the activation scale
-// sA(i,kb) is then one register per lane and slice, and for the 128x128-block weight
-// scales of FWD/DGRAD the whole scale product is a single multiply per lane and slice.
+// Kernel shape (one workgroup = 512 threads = 8 waves, one 256x256 output tile):
+//  * K loop over 128-deep slices, double-buffered in LDS (2 x 66 KB): the next slice's
+//    A and B tiles (256 x 128 bytes each) and its scales are copied HBM/L2 -> LDS with
+//    global_load_lds_dwordx4 (no VGPR round trip) while the current slice is multiplied.
+//  * LDS rows are 128 bytes = 8 chunks of 16 bytes; chunk c of row r is stored at
+//    position c ^ ((r >> 1) & 7) so that the fragment reads of 16 consecutive rows spread
+//    over all 64 LDS banks.  The swizzle is applied on the global side: the lane that
+//    lands at position p fetches logical chunk p ^ ((r >> 1) & 7).
+//  * Waves form a 4 (M) x 2 (N) grid of 64 x 128 wave tiles: 2 x 4 MFMA tiles of 32x32,
+//    128 fp32 accumulator registers per lane.
+//  * Operand roles inside the MFMA are swapped (the B fragment is the instruction's A
+//    operand) so that every lane owns ONE output row and 16 output columns: the row
+//    scale sA(i,kb) is one register per lane and slice; with 128x128 weight blocks
+//    (FWD/DGRAD) the whole scale product is one multiply per lane and slice, and the
+//    promotion is one FMA per accumulator element per slice.
+//  * Tiles are visited in an XCD-aware order: the dispatcher places workgroup b on XCD
+//    b % 8, so each XCD is given a contiguous run of tiles, walked in groups of 8 tile
+//    rows, so that the tiles resident in one XCD's L2 share A rows and B columns.
+//  * The epilogue stages each wave's output tile in LDS and writes whole row segments
+//    with 16-byte stores (a lane's own fragment holds 4 columns of 16 rows).
+//  * M or N that are multiples of 128 but not of 256 leave half-empty edge tiles: their
+//    loads are clamped to valid rows and their stores are masked.
 #include <hip/hip_runtime.h>
 
 #include "internal.hpp"
@@ -23,6 +41,14 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef uint32_t g_u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t g_u32x2 __attribute__((ext_vector_type(2)));
 typedef float g_f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void glb_void;
+
+constexpr int kBM = 256, kBN = 256, kBK = 128;
+constexpr int kThreads = 512;
+constexpr int kStageA = kBM * kBK;              // 32 KB
+constexpr int kStageB = kBN * kBK;              // 32 KB
+constexpr int kStageBytes = kStageA + kStageB + 1024 + 1024;   // + sA tile + sB tile (fp32 x 256)
 
 // D = X * Y + Cin for X: 32x64 (lanes index rows), Y: 64x32 (lanes index columns), E4M3.
 // Zero scale operands select the unscaled instruction.
@@ -43,145 +69,255 @@ __device__ __forceinline__ v8i join(g_u32x4 a, g_u32x4 b) {
   return r;
 }
 
-// 16-byte chunk swizzle of a [rows][128 B] LDS tile: chunk c of row r lives at c ^ (r & 7),
-// so 8 consecutive rows reading the same logical chunk hit 8 different bank groups.
-__device__ __forceinline__ int swz(int r, int c) { return c ^ (r & 7); }
+__device__ __forceinline__ void g2lds16(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds((glb_void*)g, (lds_void*)lds, 16, 0, 0);
+}
+__device__ __forceinline__ void g2lds4(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds((glb_void*)g, (lds_void*)lds, 4, 0, 0);
+}
 
-// ---------------------------------------------------------------------------------------
-// v0: 128x128 block tile, 4 waves in a 2x2 grid of 64x64 wave tiles (2x2 MFMA tiles of
-// 32x32 each), one 128-deep slice per step; the next slice is prefetched into registers
-// while the current one is multiplied.
-// ---------------------------------------------------------------------------------------
+struct GemmArgs {
+  int M, N, K;
+  int tiles_m, tiles_n;
+  const uint8_t* A;
+  int64_t lda;
+  const float* sA;
+  const uint8_t* B;
+  int64_t ldb;
+  const float* sB;
+  void* C;
+  int64_t ldc;
+};
+
+// Map the linear workgroup id to a (tile_m, tile_n) pair: XCD-contiguous, grouped rows.
+__device__ __forceinline__ void tile_of(int b, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int nt = tiles_m * tiles_n;
+  const int full = (nt >> 3) << 3;
+  int logical = b;
+  if (b < full) logical = (b & 7) * (nt >> 3) + (b >> 3);
+  constexpr int kGroup = 8;
+  const int per_group = kGroup * tiles_n;
+  const int g = logical / per_group;
+  const int first_m = g * kGroup;
+  const int gsize = min(tiles_m - first_m, kGroup);
+  const int r = logical - g * per_group;
+  tm = first_m + r % gsize;
+  tn = r / gsize;
+}
+
+// Swizzled position of 16-byte chunk c in a 128-byte LDS row r.  Consecutive row pairs
+// share a 256-byte bank line (64 banks x 4 bytes); XOR-ing the chunk with (r >> 1) & 7 spreads
+// the 16 rows that one ds_read_b128 quarter-wave touches over all 64 banks.
+__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 7); }
+
 template <int MODE, bool OUT_BF16>
-__global__ __launch_bounds__(256) void gemm_v0_kernel(int M, int N, int K, const uint8_t* __restrict__ A,
-                                                      int64_t lda, const float* __restrict__ sA,
-                                                      const uint8_t* __restrict__ B, int64_t ldb,
-                                                      const float* __restrict__ sB, void* __restrict__ Cv,
-                                                      int64_t ldc) {
-  __shared__ __attribute__((aligned(16))) uint8_t As[128 * 128];
-  __shared__ __attribute__((aligned(16))) uint8_t Bs[128 * 128];
+__global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
   const int t = threadIdx.x;
   const int lane = t & 63;
-  const int wave = t >> 6;
+  // wave index as a wave-uniform (scalar) value, so per-wave pointers live in SGPRs
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const int m0 = blockIdx.y * 128, n0 = blockIdx.x * 128;
-  const int nk = K >> 7;
-  const int gc = t & 7, gr = t >> 3;
-  const uint8_t* Ag = A + (int64_t)(m0 + gr) * lda + gc * 16;
-  const uint8_t* Bg = B + (int64_t)(n0 + gr) * ldb + gc * 16;
   const int l32 = lane & 31, h = lane >> 5;
+  int tm, tn;
+  tile_of(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
+  const int m0 = tm * kBM, n0 = tn * kBN;
+  const int nk = p.K / kBK;
 
-  g_u32x4 ra[4], rb[4];
+  // ---- global -> LDS copy plan.  Wave w moves rows 32w .. 32w+31 of the A and B tiles as
+  // four 8-row groups; one global_load_lds_dwordx4 moves one group (64 lanes x 16 bytes).
+  // The group's first row is wave-uniform (clamped as a whole: M - m0 is a multiple of 128,
+  // so a group is either entirely inside or entirely outside the matrix), and each lane
+  // adds its own row-in-group and swizzled chunk.
+  const int crow = lane >> 3;
+  const uint8_t* a_grp[4];
+  const uint8_t* b_grp[4];
 #pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    ra[p] = *reinterpret_cast<const g_u32x4*>(Ag + (int64_t)p * 32 * lda);
-    rb[p] = *reinterpret_cast<const g_u32x4*>(Bg + (int64_t)p * 32 * ldb);
+  for (int q = 0; q < 4; ++q) {
+    const int r0 = wave * 32 + q * 8;
+    a_grp[q] = p.A + (int64_t)min(m0 + r0, p.M - 8) * p.lda;
+    b_grp[q] = p.B + (int64_t)min(n0 + r0, p.N - 8) * p.ldb;
   }
+  // The lane lands at physical chunk (lane & 7) of row r = 32 wave + 8 q + crow and fetches the
+  // logical chunk stored there, swz(r, lane & 7); (r >> 1) & 7 = (4 q + (crow >> 1)) & 7, so
+  // even and odd groups q need different lane offsets.
+  uint32_t a_off[2], b_off[2];
+#pragma unroll
+  for (int qp = 0; qp < 2; ++qp) {
+    const uint32_t ch = (uint32_t)(swz(qp * 8 + crow, lane & 7) << 4);
+    a_off[qp] = (uint32_t)(crow * p.lda) + ch;
+    b_off[qp] = (uint32_t)(crow * p.ldb) + ch;
+  }
+  // scale tiles travel with the operand tiles, so one wait covers a whole slice:
+  //   wave 0: sA[kb][m0 .. m0+255] (4 floats per lane);
+  //   wave 1: WGRAD sB[kb][n0 .. n0+255]; FWD/DGRAD the two 128-block weight scales
+  //           sB[n0/128 + l][kb] (lanes 0 and 1; the other lanes repeat lane 1's address).
+  const int s_m = min(m0 + lane * 4, p.M - 4);
+  const int s_n = min(n0 + lane * 4, p.N - 4);
+  const int64_t s_blk = (int64_t)min((n0 >> 7) + min(lane, 1), (p.N >> 7) - 1) * nk;
 
-  v16f acc[2][2];
+  auto issue_slice = [&](int kb, int stage) {
+    uint8_t* st = smem + stage * kStageBytes;
+    const int64_t ko = (int64_t)kb * kBK;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      g2lds16(a_grp[q] + ko + a_off[q & 1], st + (wave * 32 + q * 8) * kBK);
+      g2lds16(b_grp[q] + ko + b_off[q & 1], st + kStageA + (wave * 32 + q * 8) * kBK);
+    }
+    if (wave == 0) g2lds16(p.sA + (int64_t)kb * p.M + s_m, st + kStageA + kStageB);
+    if (wave == 1) {
+      if (MODE == 2)
+        g2lds16(p.sB + (int64_t)kb * p.N + s_n, st + kStageA + kStageB + 1024);
+      else
+        g2lds4(p.sB + s_blk + kb, st + kStageA + kStageB + 1024);
+    }
+  };
+
+  v16f acc[2][4];
 #pragma unroll
   for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < 2; ++ni)
+    for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.0f;
-  const v16f zero = acc[0][0];
+  v16f zero;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) zero[v] = 0.0f;
+
+  // fragment reads: lane reads 64 bytes (chunks 4h .. 4h+3) of row r; the swizzle term of
+  // every row this lane reads is (l32 >> 1) & 7 (tile row offsets are multiples of 32)
+  const int fsw = (l32 >> 1) & 7;
+  const int fcol[4] = {((4 * h + 0) ^ fsw) << 4, ((4 * h + 1) ^ fsw) << 4, ((4 * h + 2) ^ fsw) << 4,
+                       ((4 * h + 3) ^ fsw) << 4};
+
+  issue_slice(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
 
   for (int kb = 0; kb < nk; ++kb) {
-    __syncthreads();
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int r = gr + 32 * p;
-      *reinterpret_cast<g_u32x4*>(As + r * 128 + swz(r, gc) * 16) = ra[p];
-      *reinterpret_cast<g_u32x4*>(Bs + r * 128 + swz(r, gc) * 16) = rb[p];
-    }
-    __syncthreads();
-    if (kb + 1 < nk) {
-      const int64_t ko = (int64_t)(kb + 1) * 128;
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        ra[p] = *reinterpret_cast<const g_u32x4*>(Ag + (int64_t)p * 32 * lda + ko);
-        rb[p] = *reinterpret_cast<const g_u32x4*>(Bg + (int64_t)p * 32 * ldb + ko);
-      }
-    }
+    const int stage = kb & 1;
+    if (kb + 1 < nk) issue_slice(kb + 1, stage ^ 1);
+    const uint8_t* st = smem + stage * kStageBytes;
+    const uint8_t* As = st + (wm * 64 + l32) * kBK;
+    const uint8_t* Bs = st + kStageA + (wn * 128 + l32) * kBK;
+    const float* sAs = reinterpret_cast<const float*>(st + kStageA + kStageB);
+    const float* sBs = reinterpret_cast<const float*>(st + kStageA + kStageB + 1024);
 
-    float sa[2];
+    // FWD/DGRAD: the wave's 128 columns lie in one 128-column weight block (index wn)
+    const float sbb = (MODE != 2) ? sBs[wn] : 1.0f;
+    float sc[2];
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi) sa[mi] = sA[(int64_t)kb * M + m0 + wm * 64 + mi * 32 + l32];
-    float sbb = 0.0f;
-    g_f32x4 sbw[2][4];
-    if (MODE != 2) {
-      sbb = sB[(int64_t)(n0 >> 7) * (K >> 7) + kb];
-    } else {
-#pragma unroll
-      for (int ni = 0; ni < 2; ++ni)
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-          sbw[ni][g] = *reinterpret_cast<const g_f32x4*>(sB + (int64_t)kb * N + n0 + wn * 64 + ni * 32 + 8 * g + 4 * h);
-    }
+    for (int mi = 0; mi < 2; ++mi) sc[mi] = sAs[wm * 64 + mi * 32 + l32] * sbb;
 
-    v8i af[2][2], bf[2][2];
-#pragma unroll
-    for (int mi = 0; mi < 2; ++mi) {
-      const int r = wm * 64 + mi * 32 + l32;
+    auto frag = [&](const uint8_t* rowp, v8i& f0, v8i& f1) {
       g_u32x4 c[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) c[j] = *reinterpret_cast<const g_u32x4*>(As + r * 128 + swz(r, 4 * h + j) * 16);
-      af[mi][0] = join(c[0], c[1]);
-      af[mi][1] = join(c[2], c[3]);
-    }
+      for (int j = 0; j < 4; ++j) c[j] = *reinterpret_cast<const g_u32x4*>(rowp + fcol[j]);
+      f0 = join(c[0], c[1]);
+      f1 = join(c[2], c[3]);
+    };
+    v8i af[2][2];
 #pragma unroll
-    for (int ni = 0; ni < 2; ++ni) {
-      const int r = wn * 64 + ni * 32 + l32;
-      g_u32x4 c[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) c[j] = *reinterpret_cast<const g_u32x4*>(Bs + r * 128 + swz(r, 4 * h + j) * 16);
-      bf[ni][0] = join(c[0], c[1]);
-      bf[ni][1] = join(c[2], c[3]);
-    }
+    for (int mi = 0; mi < 2; ++mi) frag(As + mi * 32 * kBK, af[mi][0], af[mi][1]);
 
+    // 8 MFMA tiles per slice (column-tile major), software-pipelined.  Step s issues, in
+    // this order: half of the next column tile's B-fragment reads (prefetch), the two MFMAs
+    // of tile s, and the 16 promotion FMAs of tile s-1.  Every LDS wait then covers reads
+    // issued a full step earlier.  (WGRAD reads its 16 column scales per tile instead of
+    // prefetching, to stay within 256 VGPRs.)
+    constexpr bool kPrefetchB = MODE != 2;
+    v8i bc[2], bn[2];
+    frag(Bs, bc[0], bc[1]);
+    g_u32x4 nc[4];
+    v16f pr[2];
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi) {
-#pragma unroll
-      for (int ni = 0; ni < 2; ++ni) {
-        v16f p = mfma_32x32x64_e4m3(bf[ni][0], af[mi][0], zero);
-        p = mfma_32x32x64_e4m3(bf[ni][1], af[mi][1], p);
-        if (MODE != 2) {
-          const float sc = sa[mi] * sbb;
-#pragma unroll
-          for (int v = 0; v < 16; ++v) acc[mi][ni][v] = __builtin_fmaf(p[v], sc, acc[mi][ni][v]);
-        } else {
-#pragma unroll
-          for (int v = 0; v < 16; ++v)
-            acc[mi][ni][v] = __builtin_fmaf(p[v], sa[mi] * sbw[ni][v >> 2][v & 3], acc[mi][ni][v]);
+    for (int s = 0; s <= 8; ++s) {
+      if (s < 8) {
+        const int ni = s >> 1, mi = s & 1;
+        if (kPrefetchB && ni < 3) {
+          const uint8_t* rowp = Bs + (ni + 1) * 32 * kBK;
+          nc[2 * mi + 0] = *reinterpret_cast<const g_u32x4*>(rowp + fcol[2 * mi + 0]);
+          nc[2 * mi + 1] = *reinterpret_cast<const g_u32x4*>(rowp + fcol[2 * mi + 1]);
+        }
+        if (!kPrefetchB && mi == 0 && ni > 0) frag(Bs + ni * 32 * kBK, bc[0], bc[1]);
+        pr[s & 1] = mfma_32x32x64_e4m3(bc[0], af[mi][0], zero);
+        pr[s & 1] = mfma_32x32x64_e4m3(bc[1], af[mi][1], pr[s & 1]);
+        if (kPrefetchB && mi == 1 && ni < 3) {
+          bc[0] = join(nc[0], nc[1]);
+          bc[1] = join(nc[2], nc[3]);
         }
       }
+      if (s > 0) {
+        const int q = s - 1, ni = q >> 1, mi = q & 1;
+        const v16f& pq = pr[q & 1];
+        if (MODE != 2) {
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc[mi][ni][v] = __builtin_fmaf(pq[v], sc[mi], acc[mi][ni][v]);
+        } else {
+          const float* sbp = sBs + wn * 128 + ni * 32 + 4 * h;
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const g_f32x4 sbw = *reinterpret_cast<const g_f32x4*>(sbp + 8 * g);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              acc[mi][ni][4 * g + e] = __builtin_fmaf(pq[4 * g + e], sc[mi] * sbw[e], acc[mi][ni][4 * g + e]);
+          }
+        }
+      }
+      // hard fence: nothing moves across steps, so prefetch reads stay one step ahead
+      __builtin_amdgcn_sched_barrier(0);
     }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
   }
 
-  // Epilogue: lane owns row i, columns j0 + 8g + {0..3}.
+  // ---- epilogue through LDS (free after the loop's last barrier): each wave stages its own
+  // output tile, one 32-row half at a time, in a private LDS region with a padded row stride
+  // (272 B for bf16, 528 B for fp32: rows land 4 banks apart), then writes whole 256 / 512-
+  // byte row segments with 16-byte stores.  The fp32 regions of the 8 waves take exactly the
+  // 2 x 66 KB the main loop used.
+  const bool rows_ok = m0 + wm * 64 < p.M;
+  const bool cols_ok = n0 + wn * 128 < p.N;
+  constexpr int kEs = OUT_BF16 ? 2 : 4;                  // output element size
+  constexpr int kRow = 128 * kEs + 16;                   // staged row stride (bytes)
+  constexpr int kLanesPerRow = 128 * kEs / 16;           // 16 (bf16) or 32 (fp32)
+  constexpr int kRowsPerIt = 64 / kLanesPerRow;
+  static_assert(8 * 32 * kRow <= 2 * kStageBytes, "epilogue staging exceeds the LDS allocation");
+  uint8_t* wbuf = smem + wave * (32 * kRow);
+  const int rr = lane / kLanesPerRow, rc = lane % kLanesPerRow;
 #pragma unroll
   for (int mi = 0; mi < 2; ++mi) {
-    const int64_t i = m0 + wm * 64 + mi * 32 + l32;
 #pragma unroll
-    for (int ni = 0; ni < 2; ++ni) {
-      const int64_t j0 = n0 + wn * 64 + ni * 32 + 4 * h;
+    for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int64_t j = j0 + 8 * g;
+        uint8_t* dst = wbuf + l32 * kRow + (ni * 32 + 8 * g + 4 * h) * kEs;
         if (OUT_BF16) {
           g_u32x2 o;
           o[0] = bf16_rne(acc[mi][ni][4 * g + 0]) | (bf16_rne(acc[mi][ni][4 * g + 1]) << 16);
           o[1] = bf16_rne(acc[mi][ni][4 * g + 2]) | (bf16_rne(acc[mi][ni][4 * g + 3]) << 16);
-          *reinterpret_cast<g_u32x2*>(static_cast<uint16_t*>(Cv) + i * ldc + j) = o;
+          *reinterpret_cast<g_u32x2*>(dst) = o;
         } else {
-          g_f32x4 o = {acc[mi][ni][4 * g + 0], acc[mi][ni][4 * g + 1], acc[mi][ni][4 * g + 2],
-                       acc[mi][ni][4 * g + 3]};
-          *reinterpret_cast<g_f32x4*>(static_cast<float*>(Cv) + i * ldc + j) = o;
+          const g_f32x4 o = {acc[mi][ni][4 * g + 0], acc[mi][ni][4 * g + 1], acc[mi][ni][4 * g + 2],
+                             acc[mi][ni][4 * g + 3]};
+          *reinterpret_cast<g_f32x4*>(dst) = o;
         }
       }
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_wave_barrier();
+    if (rows_ok && cols_ok) {
+      uint8_t* cbase = static_cast<uint8_t*>(p.C) +
+                       ((int64_t)(m0 + wm * 64 + mi * 32) * p.ldc + n0 + wn * 128) * kEs;
+#pragma unroll
+      for (int it = 0; it < 32 / kRowsPerIt; ++it) {
+        const int r = it * kRowsPerIt + rr;
+        const g_u32x4 v = *reinterpret_cast<const g_u32x4*>(wbuf + r * kRow + rc * 16);
+        *reinterpret_cast<g_u32x4*>(cbase + (int64_t)r * p.ldc * kEs + rc * 16) = v;
+      }
     }
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_wave_barrier();
   }
 }
 
@@ -196,17 +332,17 @@ __global__ __launch_bounds__(256) void zero_fill_kernel(void* __restrict__ C, in
 
 size_t gemm_workspace_bytes(int, int64_t, int64_t, int64_t) { return 0; }
 
-template <int MODE>
-static hipError_t launch_mode(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
-                              const float* sA, const uint8_t* B, int64_t ldb, const float* sB,
-                              void* C, int64_t ldc, bool out_bf16, hipStream_t st) {
-  const dim3 grid((unsigned)(N / 128), (unsigned)(M / 128));
-  if (out_bf16)
-    hipLaunchKernelGGL((gemm_v0_kernel<MODE, true>), grid, dim3(256), 0, st, (int)M, (int)N, (int)K, A,
-                       lda, sA, B, ldb, sB, C, ldc);
-  else
-    hipLaunchKernelGGL((gemm_v0_kernel<MODE, false>), grid, dim3(256), 0, st, (int)M, (int)N, (int)K, A,
-                       lda, sA, B, ldb, sB, C, ldc);
+template <int MODE, bool BF16>
+static hipError_t launch_one(const GemmArgs& a, hipStream_t st) {
+  const int smem = 2 * kStageBytes;
+  static bool attr_set = false;   // benign race: the attribute value is the same for every caller
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<MODE, BF16>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, smem);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((gemm_kernel<MODE, BF16>), dim3(a.tiles_m * a.tiles_n), dim3(kThreads), smem, st, a);
   return hipGetLastError();
 }
 
@@ -219,11 +355,19 @@ hipError_t launch_gemm(int mode, int64_t M, int64_t N, int64_t K, const uint8_t*
     hipLaunchKernelGGL(zero_fill_kernel, dim3(8, (unsigned)gy), dim3(256), 0, st, C, M, N * es, ldc * es);
     return hipGetLastError();
   }
-  if (N / 128 > 0x7FFFFFFF || M / 128 > 65535) return hipErrorInvalidConfiguration;
-  switch (mode) {
-    case 0: return launch_mode<0>(M, N, K, A, lda, sA, B, ldb, sB, C, ldc, out_bf16, st);
-    case 1: return launch_mode<1>(M, N, K, A, lda, sA, B, ldb, sB, C, ldc, out_bf16, st);
-    default: return launch_mode<2>(M, N, K, A, lda, sA, B, ldb, sB, C, ldc, out_bf16, st);
+  GemmArgs a;
+  a.M = (int)M; a.N = (int)N; a.K = (int)K;
+  a.tiles_m = (int)((M + kBM - 1) / kBM);
+  a.tiles_n = (int)((N + kBN - 1) / kBN);
+  if ((int64_t)a.tiles_m * a.tiles_n > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  a.A = A; a.lda = lda; a.sA = sA; a.B = B; a.ldb = ldb; a.sB = sB; a.C = C; a.ldc = ldc;
+  switch (mode * 2 + (out_bf16 ? 1 : 0)) {
+    case 0: return launch_one<0, false>(a, st);
+    case 1: return launch_one<0, true>(a, st);
+    case 2: return launch_one<1, false>(a, st);
+    case 3: return launch_one<1, true>(a, st);
+    case 4: return launch_one<2, false>(a, st);
+    default: return launch_one<2, true>(a, st);
   }
 }
 

@@ -8,8 +8,8 @@ under the loose one: 1e-4 normalized for the fp32 accumulator.  (Measured on MI3
 the FP8 MFMA's own accumulation of a 128-deep slice stays within ~3.5e-5 normalized on
 wide-dynamic-range random codes; the fp32 promotion adds ~K/128 * 2^-24.)
 
-bf16 outputs add the epilogue's own rounding, at most 2^-9 |C| (RNE).  On realistic
-workloads (the named workloads below) that is ~1e-5 normalized and the plain bar is
+bf16 outputs add the epilogue's own rounding, at most 2^-8 |C| (RNE, 8-bit significand).  On realistic
+workloads (the named workloads below) that stays below ~5e-4 normalized and the plain bar is
 asserted on the bf16 output.  The random-code cases use log-uniform code magnitudes
 and scales spread over 2^30, so one product can carry a whole row (|C| close to
 ||A_i|| ||B_j||); there the bf16 output is checked against the bar plus one bf16
@@ -67,16 +67,16 @@ def run_gpu(P, mode, A, sA, B, sB, out_dtype, lda_pad=0, ldc_pad=0):
 
 
 def check(P, mode, A, sA, B, sB, out_dtype, what, bf16_allowance=False, **kw):
-    """bf16_allowance: add one bf16 rounding of C_ref (2^-9 |C_ref|) to both bounds."""
+    """bf16_allowance: add one bf16 rounding of C_ref (2^-8 |C_ref|) to the 1e-3 bar."""
     say(f"[gemm] {what} mode={mode} M,N,K={A.shape[0]},{B.shape[0]},{A.shape[1]} out={'bf16' if out_dtype == 0 else 'fp32'} {kw}")
     C = run_gpu(P, mode, A, sA, B, sB, out_dtype, **kw)
     ref = gemm.gemm(mode, A, sA, B, sB)
     na, nb = gemm.operand_norms(mode, A, sA, B, sB)
     err, diff, den = normalized_error(C, ref, na, nb)
     say(f"    max normalized error {err:.3e}")
-    extra = 2.0 ** -9 * np.abs(ref) * (1 + 2.0 ** -7) if (out_dtype == 0 and bf16_allowance) else 0.0
+    extra = 2.0 ** -8 * np.abs(ref) * (1 + 2.0 ** -7) if (out_dtype == 0 and bf16_allowance) else 0.0
     assert (diff <= TOL * den + extra).all(), err
-    bound = TIGHT * den + (2.0 ** -9 * np.abs(ref) * (1 + 2.0 ** -7) if out_dtype == 0 else 0.0)
+    bound = TIGHT * den + (2.0 ** -8 * np.abs(ref) * (1 + 2.0 ** -7) if out_dtype == 0 else 0.0)
     worst = np.unravel_index(np.argmax(diff - bound), diff.shape)
     assert (diff <= bound).all(), (worst, C[worst], ref[worst], den[worst])
     return C, ref
@@ -225,7 +225,7 @@ def sampled_check(P, mode, A, sA, B, sB, out_dtype, what, n=256, seed=0):
     err, diff, den = normalized_error(sub, ref, na, nb)
     say(f"    max normalized error {err:.3e}")
     assert err <= TOL
-    bound = TIGHT * den + (2.0 ** -9 * np.abs(ref) * (1 + 2.0 ** -7) if out_dtype == 0 else 0.0)
+    bound = TIGHT * den + (2.0 ** -8 * np.abs(ref) * (1 + 2.0 ** -7) if out_dtype == 0 else 0.0)
     assert (diff <= bound).all()
     assert np.isfinite(C).all()
 
