@@ -32,7 +32,10 @@
 //    loads are clamped to valid rows and their stores are masked.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "internal.hpp"
+#include "gemm_slice_asm.inc"
 
 namespace puro {
 
@@ -56,10 +59,12 @@ __device__ __forceinline__ v16f mfma_32x32x64_e4m3(v8i x, v8i y, v16f c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(x, y, c, 0, 0, 0, 0, 0, 0);
 }
 
-__device__ __forceinline__ uint32_t bf16_rne(float f) {
-  const uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;   // quiet NaN
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+// Two fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32), packed low | high << 16.
+typedef __bf16 g_bf16x2 __attribute__((ext_vector_type(2)));
+typedef float g_f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
+  const g_f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, g_bf16x2));
 }
 
 __device__ __forceinline__ v8i join(g_u32x4 a, g_u32x4 b) {
@@ -67,6 +72,11 @@ __device__ __forceinline__ v8i join(g_u32x4 a, g_u32x4 b) {
   r[0] = (int)a[0]; r[1] = (int)a[1]; r[2] = (int)a[2]; r[3] = (int)a[3];
   r[4] = (int)b[0]; r[5] = (int)b[1]; r[6] = (int)b[2]; r[7] = (int)b[3];
   return r;
+}
+
+// 32-bit LDS byte address of a pointer into shared memory
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
 __device__ __forceinline__ void g2lds16(const void* g, void* lds) {
@@ -79,6 +89,9 @@ __device__ __forceinline__ void g2lds4(const void* g, void* lds) {
 struct GemmArgs {
   int M, N, K;
   int tiles_m, tiles_n;
+  int splits;            // contraction split: block b works on split b / (tiles_m * tiles_n)
+  int kb_per_split;      // 128-deep slices per split
+  int64_t split_stride;  // elements between the fp32 partial outputs of consecutive splits
   const uint8_t* A;
   int64_t lda;
   const float* sA;
@@ -121,9 +134,13 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
   const int wm = wave >> 1, wn = wave & 1;
   const int l32 = lane & 31, h = lane >> 5;
   int tm, tn;
-  tile_of(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
+  const int ntiles = p.tiles_m * p.tiles_n;
+  const int split = blockIdx.x / ntiles;
+  tile_of(blockIdx.x - split * ntiles, p.tiles_m, p.tiles_n, tm, tn);
   const int m0 = tm * kBM, n0 = tn * kBN;
-  const int nk = p.K / kBK;
+  const int nk = p.K / kBK;                       // slices of the whole contraction
+  const int kb_begin = split * p.kb_per_split;    // this block's slice range
+  const int kb_end = min(kb_begin + p.kb_per_split, nk);
 
   // ---- global -> LDS copy plan.  Wave w moves rows 32w .. 32w+31 of the A and B tiles as
   // four 8-row groups; one global_load_lds_dwordx4 moves one group (64 lanes x 16 bytes).
@@ -157,14 +174,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
   const int s_n = min(n0 + lane * 4, p.N - 4);
   const int64_t s_blk = (int64_t)min((n0 >> 7) + min(lane, 1), (p.N >> 7) - 1) * nk;
 
-  auto issue_slice = [&](int kb, int stage) {
+  auto issue_scales = [&](int kb, int stage) {
     uint8_t* st = smem + stage * kStageBytes;
-    const int64_t ko = (int64_t)kb * kBK;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      g2lds16(a_grp[q] + ko + a_off[q & 1], st + (wave * 32 + q * 8) * kBK);
-      g2lds16(b_grp[q] + ko + b_off[q & 1], st + kStageA + (wave * 32 + q * 8) * kBK);
-    }
     if (wave == 0) g2lds16(p.sA + (int64_t)kb * p.M + s_m, st + kStageA + kStageB);
     if (wave == 1) {
       if (MODE == 2)
@@ -173,14 +184,23 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
         g2lds4(p.sB + s_blk + kb, st + kStageA + kStageB + 1024);
     }
   };
+  auto issue_slice = [&](int kb, int stage) {
+    uint8_t* st = smem + stage * kStageBytes;
+    const int64_t ko = (int64_t)kb * kBK;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      g2lds16(a_grp[q] + ko + a_off[q & 1], st + (wave * 32 + q * 8) * kBK);
+      g2lds16(b_grp[q] + ko + b_off[q & 1], st + kStageA + (wave * 32 + q * 8) * kBK);
+    }
+    issue_scales(kb, stage);
+  };
 
-  v16f acc[2][4];
+  // accumulator of output tile (row group mi, column tile ni) is acc[2 * ni + mi]
+  v16f acc[8];
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
+  for (int T = 0; T < 8; ++T)
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.0f;
+    for (int v = 0; v < 16; ++v) acc[T][v] = 0.0f;
   v16f zero;
 #pragma unroll
   for (int v = 0; v < 16; ++v) zero[v] = 0.0f;
@@ -191,13 +211,18 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
   const int fcol[4] = {((4 * h + 0) ^ fsw) << 4, ((4 * h + 1) ^ fsw) << 4, ((4 * h + 2) ^ fsw) << 4,
                        ((4 * h + 3) ^ fsw) << 4};
 
-  issue_slice(0, 0);
+  // FWD/DGRAD: product of the last tile of a slice, promoted by the next slice's block
+  v16f pcarry = zero;
+  float scp = 0.0f;
+
+  issue_slice(kb_begin, 0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  for (int kb = 0; kb < nk; ++kb) {
-    const int stage = kb & 1;
-    if (kb + 1 < nk) issue_slice(kb + 1, stage ^ 1);
+  for (int kb = kb_begin; kb < kb_end; ++kb) {
+    const int stage = (kb - kb_begin) & 1;
+    // (FWD/DGRAD: the operand copy of the next slice is issued inside the asm block)
+    if (MODE == 2 && kb + 1 < kb_end) issue_slice(kb + 1, stage ^ 1);
     const uint8_t* st = smem + stage * kStageBytes;
     const uint8_t* As = st + (wm * 64 + l32) * kBK;
     const uint8_t* Bs = st + kStageA + (wn * 128 + l32) * kBK;
@@ -210,67 +235,100 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
 #pragma unroll
     for (int mi = 0; mi < 2; ++mi) sc[mi] = sAs[wm * 64 + mi * 32 + l32] * sbb;
 
-    auto frag = [&](const uint8_t* rowp, v8i& f0, v8i& f1) {
-      g_u32x4 c[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) c[j] = *reinterpret_cast<const g_u32x4*>(rowp + fcol[j]);
-      f0 = join(c[0], c[1]);
-      f1 = join(c[2], c[3]);
-    };
-    v8i af[2][2];
-#pragma unroll
-    for (int mi = 0; mi < 2; ++mi) frag(As + mi * 32 * kBK, af[mi][0], af[mi][1]);
+    if constexpr (MODE != 2) {
+      // hand-scheduled slice (gemm_slice_asm.inc): LDS byte addresses of this lane's four
+      // swizzled 16-byte chunks in its A row and in its B row of the current stage
+      const uint32_t sbase = lds_addr(st);
+      const uint32_t arow = sbase + (uint32_t)((wm * 64 + l32) * kBK);
+      const uint32_t brow = sbase + (uint32_t)(kStageA + (wn * 128 + l32) * kBK);
+      const float sc0 = sc[0], sc1 = sc[1];
+      // next slice (the last slice re-copies itself into the idle stage, so the block has
+      // no branch); its scales are copied here, after this slice's scales were read
+      const int kn = kb + 1 < kb_end ? kb + 1 : kb;
+      if (kb + 1 < kb_end) issue_scales(kb + 1, stage ^ 1);
+      const int64_t ko = (int64_t)kn * kBK;
+      const uint32_t m0 = lds_addr(smem + (stage ^ 1) * kStageBytes) + (uint32_t)(wave * 32 * kBK);
+      asm volatile(PURO_SLICE_ASM_ROWSCALE
+                   : "+{v[0:15]}"(acc[0]), "+{v[16:31]}"(acc[1]), "+{v[32:47]}"(acc[2]), "+{v[48:63]}"(acc[3]),
+                     "+{v[64:79]}"(acc[4]), "+{v[80:95]}"(acc[5]), "+{v[96:111]}"(acc[6]), "+{v[112:127]}"(acc[7]),
+                     "+{v[144:159]}"(pcarry)
+                   : [aj0] "v"(arow + fcol[0]), [aj1] "v"(arow + fcol[1]), [aj2] "v"(arow + fcol[2]),
+                     [aj3] "v"(arow + fcol[3]), [bj0] "v"(brow + fcol[0]), [bj1] "v"(brow + fcol[1]),
+                     [bj2] "v"(brow + fcol[2]), [bj3] "v"(brow + fcol[3]), [sc0] "v"(sc0), [sc1] "v"(sc1),
+                     [scp] "v"(scp),
+                     [ga0] "s"(a_grp[0] + ko), [ga1] "s"(a_grp[1] + ko), [ga2] "s"(a_grp[2] + ko),
+                     [ga3] "s"(a_grp[3] + ko), [gb0] "s"(b_grp[0] + ko), [gb1] "s"(b_grp[1] + ko),
+                     [gb2] "s"(b_grp[2] + ko), [gb3] "s"(b_grp[3] + ko), [oa0] "v"(a_off[0]), [oa1] "v"(a_off[1]),
+                     [ob0] "v"(b_off[0]), [ob1] "v"(b_off[1]), [m0] "s"(m0)
+                   : PURO_SLICE_ASM_CLOBBERS, "m0", "memory");
+      scp = sc1;  // tile 7's product stays in pcarry until the next block (or the tail)
+      continue;   // the block ended with the slice's wait and barrier
+    } else {
+      auto frag = [&](const uint8_t* rowp, v8i& f0, v8i& f1) {
+        g_u32x4 c[4];
+  #pragma unroll
+        for (int j = 0; j < 4; ++j) c[j] = *reinterpret_cast<const g_u32x4*>(rowp + fcol[j]);
+        f0 = join(c[0], c[1]);
+        f1 = join(c[2], c[3]);
+      };
+      v8i af[2][2];
+  #pragma unroll
+      for (int mi = 0; mi < 2; ++mi) frag(As + mi * 32 * kBK, af[mi][0], af[mi][1]);
 
-    // 8 MFMA tiles per slice (column-tile major), software-pipelined.  Step s issues, in
-    // this order: half of the next column tile's B-fragment reads (prefetch), the two MFMAs
-    // of tile s, and the 16 promotion FMAs of tile s-1.  Every LDS wait then covers reads
-    // issued a full step earlier.  (WGRAD reads its 16 column scales per tile instead of
-    // prefetching, to stay within 256 VGPRs.)
-    constexpr bool kPrefetchB = MODE != 2;
-    v8i bc[2], bn[2];
-    frag(Bs, bc[0], bc[1]);
-    g_u32x4 nc[4];
-    v16f pr[2];
-#pragma unroll
-    for (int s = 0; s <= 8; ++s) {
-      if (s < 8) {
-        const int ni = s >> 1, mi = s & 1;
-        if (kPrefetchB && ni < 3) {
-          const uint8_t* rowp = Bs + (ni + 1) * 32 * kBK;
-          nc[2 * mi + 0] = *reinterpret_cast<const g_u32x4*>(rowp + fcol[2 * mi + 0]);
-          nc[2 * mi + 1] = *reinterpret_cast<const g_u32x4*>(rowp + fcol[2 * mi + 1]);
-        }
-        if (!kPrefetchB && mi == 0 && ni > 0) frag(Bs + ni * 32 * kBK, bc[0], bc[1]);
-        pr[s & 1] = mfma_32x32x64_e4m3(bc[0], af[mi][0], zero);
-        pr[s & 1] = mfma_32x32x64_e4m3(bc[1], af[mi][1], pr[s & 1]);
-        if (kPrefetchB && mi == 1 && ni < 3) {
-          bc[0] = join(nc[0], nc[1]);
-          bc[1] = join(nc[2], nc[3]);
-        }
-      }
-      if (s > 0) {
-        const int q = s - 1, ni = q >> 1, mi = q & 1;
-        const v16f& pq = pr[q & 1];
-        if (MODE != 2) {
-#pragma unroll
-          for (int v = 0; v < 16; ++v) acc[mi][ni][v] = __builtin_fmaf(pq[v], sc[mi], acc[mi][ni][v]);
-        } else {
-          const float* sbp = sBs + wn * 128 + ni * 32 + 4 * h;
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const g_f32x4 sbw = *reinterpret_cast<const g_f32x4*>(sbp + 8 * g);
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              acc[mi][ni][4 * g + e] = __builtin_fmaf(pq[4 * g + e], sc[mi] * sbw[e], acc[mi][ni][4 * g + e]);
+      // 8 MFMA tiles per slice (column-tile major), software-pipelined.  Step s issues, in
+      // this order: half of the next column tile's B-fragment reads (prefetch), the two MFMAs
+      // of tile s, and the 16 promotion FMAs of tile s-1.  Every LDS wait then covers reads
+      // issued a full step earlier.  (WGRAD reads its 16 column scales per tile instead of
+      // prefetching, to stay within 256 VGPRs.)
+      constexpr bool kPrefetchB = MODE != 2;
+      v8i bc[2], bn[2];
+      frag(Bs, bc[0], bc[1]);
+      g_u32x4 nc[4];
+      v16f pr[2];
+  #pragma unroll
+      for (int s = 0; s <= 8; ++s) {
+        if (s < 8) {
+          const int ni = s >> 1, mi = s & 1;
+          if (kPrefetchB && ni < 3) {
+            const uint8_t* rowp = Bs + (ni + 1) * 32 * kBK;
+            nc[2 * mi + 0] = *reinterpret_cast<const g_u32x4*>(rowp + fcol[2 * mi + 0]);
+            nc[2 * mi + 1] = *reinterpret_cast<const g_u32x4*>(rowp + fcol[2 * mi + 1]);
+          }
+          if (!kPrefetchB && mi == 0 && ni > 0) frag(Bs + ni * 32 * kBK, bc[0], bc[1]);
+          pr[s & 1] = mfma_32x32x64_e4m3(bc[0], af[mi][0], zero);
+          pr[s & 1] = mfma_32x32x64_e4m3(bc[1], af[mi][1], pr[s & 1]);
+          if (kPrefetchB && mi == 1 && ni < 3) {
+            bc[0] = join(nc[0], nc[1]);
+            bc[1] = join(nc[2], nc[3]);
           }
         }
+        if (s > 0) {
+          const int q = s - 1, ni = q >> 1, mi = q & 1;
+          const v16f& pq = pr[q & 1];
+          if (MODE != 2) {
+  #pragma unroll
+            for (int v = 0; v < 16; ++v) acc[2 * ni + mi][v] = __builtin_fmaf(pq[v], sc[mi], acc[2 * ni + mi][v]);
+          } else {
+            const float* sbp = sBs + wn * 128 + ni * 32 + 4 * h;
+  #pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const g_f32x4 sbw = *reinterpret_cast<const g_f32x4*>(sbp + 8 * g);
+  #pragma unroll
+              for (int e = 0; e < 4; ++e)
+                acc[2 * ni + mi][4 * g + e] = __builtin_fmaf(pq[4 * g + e], sc[mi] * sbw[e], acc[2 * ni + mi][4 * g + e]);
+            }
+          }
+        }
+        // hard fence: nothing moves across steps, so prefetch reads stay one step ahead
+        __builtin_amdgcn_sched_barrier(0);
       }
-      // hard fence: nothing moves across steps, so prefetch reads stay one step ahead
-      __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
+
+  if constexpr (MODE != 2)
+    asm volatile(PURO_SLICE_ASM_ROWSCALE_TAIL : "+{v[112:127]}"(acc[7]) : "{v[144:159]}"(pcarry), [scp] "v"(scp));
 
   // ---- epilogue through LDS (free after the loop's last barrier): each wave stages its own
   // output tile, one 32-row half at a time, in a private LDS region with a padded row stride
@@ -295,12 +353,12 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
         uint8_t* dst = wbuf + l32 * kRow + (ni * 32 + 8 * g + 4 * h) * kEs;
         if (OUT_BF16) {
           g_u32x2 o;
-          o[0] = bf16_rne(acc[mi][ni][4 * g + 0]) | (bf16_rne(acc[mi][ni][4 * g + 1]) << 16);
-          o[1] = bf16_rne(acc[mi][ni][4 * g + 2]) | (bf16_rne(acc[mi][ni][4 * g + 3]) << 16);
+          o[0] = bf16x2_rne(acc[2 * ni + mi][4 * g + 0], acc[2 * ni + mi][4 * g + 1]);
+          o[1] = bf16x2_rne(acc[2 * ni + mi][4 * g + 2], acc[2 * ni + mi][4 * g + 3]);
           *reinterpret_cast<g_u32x2*>(dst) = o;
         } else {
-          const g_f32x4 o = {acc[mi][ni][4 * g + 0], acc[mi][ni][4 * g + 1], acc[mi][ni][4 * g + 2],
-                             acc[mi][ni][4 * g + 3]};
+          const g_f32x4 o = {acc[2 * ni + mi][4 * g + 0], acc[2 * ni + mi][4 * g + 1],
+                             acc[2 * ni + mi][4 * g + 2], acc[2 * ni + mi][4 * g + 3]};
           *reinterpret_cast<g_f32x4*>(dst) = o;
         }
       }
@@ -308,7 +366,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
     __builtin_amdgcn_wave_barrier();
     if (rows_ok && cols_ok) {
       uint8_t* cbase = static_cast<uint8_t*>(p.C) +
-                       ((int64_t)(m0 + wm * 64 + mi * 32) * p.ldc + n0 + wn * 128) * kEs;
+                       ((int64_t)split * p.split_stride + (int64_t)(m0 + wm * 64 + mi * 32) * p.ldc + n0 + wn * 128) * kEs;
 #pragma unroll
       for (int it = 0; it < 32 / kRowsPerIt; ++it) {
         const int r = it * kRowsPerIt + rr;
@@ -330,7 +388,56 @@ __global__ __launch_bounds__(256) void zero_fill_kernel(void* __restrict__ C, in
       reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(C) + i * ldbytes)[w] = 0u;
 }
 
-size_t gemm_workspace_bytes(int, int64_t, int64_t, int64_t) { return 0; }
+// Sum of the fp32 partials of a split contraction, in split order (deterministic), written as
+// bf16 (round to nearest even) or fp32.  4 consecutive columns per thread.
+template <bool OUT_BF16>
+__global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restrict__ part, int splits,
+                                                           int64_t split_stride, int M, int N,
+                                                           void* __restrict__ C, int64_t ldc) {
+  const int64_t n4 = N >> 2;
+  const int64_t total = (int64_t)M * n4;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t i = e / n4, j = (e - i * n4) * 4;
+    g_f32x4 acc = *reinterpret_cast<const g_f32x4*>(part + i * N + j);
+    for (int sp = 1; sp < splits; ++sp) acc += *reinterpret_cast<const g_f32x4*>(part + sp * split_stride + i * N + j);
+    if (OUT_BF16) {
+      g_u32x2 o;
+      o[0] = bf16x2_rne(acc[0], acc[1]);
+      o[1] = bf16x2_rne(acc[2], acc[3]);
+      *reinterpret_cast<g_u32x2*>(static_cast<uint16_t*>(C) + i * ldc + j) = o;
+    } else {
+      *reinterpret_cast<g_f32x4*>(static_cast<float*>(C) + i * ldc + j) = acc;
+    }
+  }
+}
+
+// Contraction split for a problem: the smallest estimated time among 1, 2, 4 and 8 splits,
+// modelling whole waves of 256 workgroups (one per CU), ~3 slices of fixed cost per
+// workgroup, and the partials' HBM round trip (~1 slice time per 10 MB).
+static int choose_splits(int64_t M, int64_t N, int64_t K) {
+  const int64_t tiles = ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
+  const int64_t nk = K / kBK;
+  int best = 1;
+  double best_t = 1e300;
+  for (int sp = 1; sp <= 8; sp *= 2) {
+    if (nk / sp < 8) break;
+    const double waves = (double)((tiles * sp + 255) / 256);
+    const double per_block = (double)((nk + sp - 1) / sp) + 3.0;
+    const double reduce = sp > 1 ? (double)(sp + 1) * M * N * 4 / 10.0e6 : 0.0;
+    const double t = waves * per_block + reduce;
+    if (t < best_t * 0.97) {
+      best_t = t;
+      best = sp;
+    }
+  }
+  return best;
+}
+
+size_t gemm_workspace_bytes(int, int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || K <= 0) return 0;
+  const int sp = choose_splits(M, N, K);
+  return sp > 1 ? (size_t)sp * (size_t)M * (size_t)N * 4 : 0;
+}
 
 template <int MODE, bool BF16>
 static hipError_t launch_one(const GemmArgs& a, hipStream_t st) {
@@ -342,13 +449,13 @@ static hipError_t launch_one(const GemmArgs& a, hipStream_t st) {
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((gemm_kernel<MODE, BF16>), dim3(a.tiles_m * a.tiles_n), dim3(kThreads), smem, st, a);
+  hipLaunchKernelGGL((gemm_kernel<MODE, BF16>), dim3(a.tiles_m * a.tiles_n * a.splits), dim3(kThreads), smem, st, a);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm(int mode, int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
                        const float* sA, const uint8_t* B, int64_t ldb, const float* sB, void* C,
-                       int64_t ldc, bool out_bf16, void*, size_t, hipStream_t st) {
+                       int64_t ldc, bool out_bf16, void* workspace, size_t workspace_bytes, hipStream_t st) {
   if (K == 0) {
     const int64_t es = out_bf16 ? 2 : 4;
     const int64_t gy = M < 65535 ? M : 65535;
@@ -361,6 +468,32 @@ hipError_t launch_gemm(int mode, int64_t M, int64_t N, int64_t K, const uint8_t*
   a.tiles_n = (int)((N + kBN - 1) / kBN);
   if ((int64_t)a.tiles_m * a.tiles_n > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   a.A = A; a.lda = lda; a.sA = sA; a.B = B; a.ldb = ldb; a.sB = sB; a.C = C; a.ldc = ldc;
+  a.splits = choose_splits(M, N, K);
+  a.kb_per_split = (int)((K / kBK + a.splits - 1) / a.splits);
+  a.split_stride = 0;
+  if (a.splits > 1) {
+    // partial sums (fp32, [split][M][N]) in the caller's workspace, then one reduction
+    if (workspace == nullptr || workspace_bytes < gemm_workspace_bytes(mode, M, N, K)) return hipErrorInvalidValue;
+    a.C = workspace;
+    a.ldc = N;
+    a.split_stride = M * N;
+    hipError_t e;
+    switch (mode) {
+      case 0: e = launch_one<0, false>(a, st); break;
+      case 1: e = launch_one<1, false>(a, st); break;
+      default: e = launch_one<2, false>(a, st); break;
+    }
+    if (e != hipSuccess) return e;
+    const int64_t work = M * (N / 4);
+    const int64_t blocks = std::min<int64_t>((work + 255) / 256, 4096);
+    if (out_bf16)
+      hipLaunchKernelGGL(split_reduce_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, st,
+                         static_cast<const float*>(workspace), a.splits, a.split_stride, (int)M, (int)N, C, ldc);
+    else
+      hipLaunchKernelGGL(split_reduce_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, st,
+                         static_cast<const float*>(workspace), a.splits, a.split_stride, (int)M, (int)N, C, ldc);
+    return hipGetLastError();
+  }
   switch (mode * 2 + (out_bf16 ? 1 : 0)) {
     case 0: return launch_one<0, false>(a, st);
     case 1: return launch_one<0, true>(a, st);

@@ -106,6 +106,14 @@ def test_gemm_validation_fp32_ld_rule():
     assert gm(ldc=258, dt=1) == LD
 
 
+def test_gemm_workspace_validation():
+    # a long contraction over few tiles needs a workspace; without one the call is refused
+    need = P.puro_fp8_gemm_workspace_size(2, 2048, 2048, 16384)
+    assert need >= 2 * 2048 * 2048 * 4
+    assert gm(mode=2, M=2048, N=2048, K=16384, lda=16384, ldb=16384, ldc=2048) == WORKSPACE
+    assert gm(mode=2, M=2048, N=2048, K=16384, lda=16384, ldb=16384, ldc=2048, ws=A16, wsb=need - 1) == WORKSPACE
+
+
 def test_workspace_query():
     for mode in (0, 1, 2):
         assert P.puro_fp8_gemm_workspace_size(mode, 0, 128, 128) == 0

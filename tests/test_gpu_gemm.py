@@ -119,6 +119,24 @@ def test_scaled_small_integers_bit_exact(P, mode):
     np.testing.assert_array_equal(C.astype(np.float64), ref)
 
 
+@pytest.mark.parametrize("mode", list(MODES))
+def test_bf16_epilogue_rounding_exact(P, mode):
+    """Exact fp32 accumulation (small integers, power-of-two scales) leaves the bf16 epilogue
+    as the only rounding: the output must be the round-to-nearest-even bf16 of the exact
+    result.  Magnitudes up to ~2^14 exercise rounding at 8 significant bits, ties included."""
+    rng = np.random.default_rng(31)
+    M, N, K = 256, 256, 512
+    small = np.array([c for c in FINITE if float(TABLE[c]).is_integer() and abs(TABLE[c]) <= 8], dtype=np.uint8)
+    A = rng.choice(small, size=(M, K)).astype(np.uint8)
+    B = rng.choice(small, size=(N, K)).astype(np.uint8)
+    sA = np.ones((K // 128, M), np.float32)
+    sB = np.ones((K // 128, N) if mode == "WGRAD" else (N // 128, K // 128), np.float32)
+    C = run_gpu(P, mode, A, sA, B, sB, 0)
+    ref = gemm.gemm(mode, A, sA, B, sB)                       # exact integers, |ref| < 2^15
+    assert (np.abs(ref) < 2 ** 24).all()
+    np.testing.assert_array_equal(C.astype(np.float64), gemm.bf16_round(ref))
+
+
 def test_one_nonzero_per_row_layout_probe(P):
     """A has one nonzero code per row at a known k; every C entry is a single scaled product.
 
@@ -170,6 +188,19 @@ def test_empty_contraction_gives_zeros(P):
     B = t.empty((128, 0), dtype=t.uint8, device="cuda")
     P.puro_fp8_gemm(0, A, None, B, None, C=C, out_dtype=1)
     assert (host(C) == 0).all()
+
+
+@pytest.mark.parametrize("mode,M,N,K,out_dtype", [("WGRAD", 512, 256, 16384, 1), ("WGRAD", 256, 384, 8192, 0),
+                                                  ("FWD", 256, 256, 8192, 0), ("DGRAD", 384, 256, 4096, 1)])
+def test_split_contraction(P, mode, M, N, K, out_dtype):
+    """Few output tiles and a long contraction: the library splits K into partial sums in the
+    workspace and reduces them in split order."""
+    assert P.puro_fp8_gemm_workspace_size(MODES[mode], M, N, K) > 0
+    A, sA, B, sB = rand_case(mode, M, N, K, seed=M + N + K)
+    check(P, mode, A, sA, B, sB, out_dtype, "split-K", bf16_allowance=True)
+    a = run_gpu(P, mode, A, sA, B, sB, out_dtype)
+    b = run_gpu(P, mode, A, sA, B, sB, out_dtype)
+    assert (a.view(np.uint32) == b.view(np.uint32)).all(), "split-K result not deterministic"
 
 
 def test_deterministic(P):
