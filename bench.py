@@ -12,10 +12,24 @@ Prints ONE JSON line.  `value` = GEMM TFLOP/s of the whole step (all 12 GEMMs' f
 divided by the step time, quantizers included in the time).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+
+HBM traffic of each kernel comes from two rocprofv3 counter runs of this script (FETCH_SIZE,
+then WRITE_SIZE), both scaled by what the same counter reads for a plain copy of known size
+that every run performs once, untimed, before the steps:
+
+    rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o pmc -- python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline
+    rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o pmc -- python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline
+    python bench.py --summarize-pmc gpurun_out/pmc_fetch gpurun_out/pmc_write   # writes TRAFFIC_FILE
+
+The summary records a hash of the kernel sources; once they change, `traffic` reads null
+until the counters are taken again.
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import statistics
@@ -29,6 +43,116 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA, TFLOP/s
 WORKLOAD = "layer_sweep_s0"
 METRIC = "FP8 blockwise GEMM TFLOP/s fwd/dgrad/wgrad (% FP8 MFMA peak); quant GB/s"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_layer_sweep_16384.txt")
+CSRC = os.path.join(ROOT, "blockwise_scaled_fp8_quant_amd", "csrc")
+COPY_BYTES = 256 << 20          # calibration copy: 256 MiB read + 256 MiB written
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        if f.endswith((".hip", ".hpp", ".cpp", ".inc", ".h")):
+            h.update(f.encode())
+            with open(os.path.join(CSRC, f), "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def op_of_kernel(name: str, last_gemm):
+    """Map a dispatched kernel's name to the bench op it belongs to (None: not a path kernel)."""
+    if "gemm_kernel<0" in name:
+        return "gemm_fwd"
+    if "gemm_kernel<1" in name:
+        return "gemm_dgrad"
+    if "gemm_kernel<2" in name:
+        return "gemm_wgrad"
+    if "split_reduce" in name or "zero_fill" in name:
+        return last_gemm
+    if "quant_1x128" in name:
+        return "quant_act_1x128"
+    if "quant_128x128" in name:
+        return "quant_w_128x128"
+    if "quant_128x1" in name:
+        return "quant_act_128x1"
+    if "neg" in name:
+        return "copy"
+    return None
+
+
+def read_counter_csv(d: str, counter: str):
+    """Per-dispatch (kernel name, value in KiB) from one rocprofv3 --pmc csv run, in dispatch order."""
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    per = {}
+    for f in files:
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] != counter:
+                    continue
+                key = int(r["Dispatch_Id"])
+                name, v = per.get(key, (r["Kernel_Name"], 0.0))
+                per[key] = (name, v + float(r["Counter_Value"]))
+    return [per[k] for k in sorted(per)]
+
+
+def summarize_pmc(fetch_dir: str, write_dir: str):
+    """Turn the two counter runs into per-op HBM bytes per launch; writes TRAFFIC_FILE."""
+    res = {}
+    factors = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = read_counter_csv(d, counter)
+        copies = [v for n, v in rows if op_of_kernel(n, None) == "copy"]
+        if not copies:
+            raise SystemExit(f"{counter}: the calibration copy was not found")
+        factors[counter] = (COPY_BYTES, copies[0] * 1024.0)
+        scale = COPY_BYTES / (copies[0] * 1024.0)
+        last = None
+        for n, v in rows:
+            op = op_of_kernel(n, last)
+            if op is None or op == "copy":
+                continue
+            if op.startswith("gemm") and "gemm_kernel" in n:
+                last = op
+            e = res.setdefault(op, {"FETCH_SIZE": 0.0, "WRITE_SIZE": 0.0, "launches": 0})
+            e[counter] += v * 1024.0 * scale
+            if counter == "FETCH_SIZE" and "split_reduce" not in n and "zero_fill" not in n:
+                e["launches"] += 1
+    lines = ["# HBM traffic per launch: layer sweep, 16384 tokens, seed 0 (bench step)",
+             "# rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o pmc -- python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline",
+             "# rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o pmc -- python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline",
+             "# python bench.py --summarize-pmc gpurun_out/pmc_fetch gpurun_out/pmc_write",
+             "# counters are scaled so that the calibration copy (256 MiB read + 256 MiB written) reads its own size;",
+             "# a GEMM op includes its split-K reduce kernel",
+             f"kernel_source_hash {kernel_source_hash()}"]
+    for c, (b, measured) in factors.items():
+        lines.append(f"calibration {c} copy_bytes {b} counter_bytes {measured:.0f} factor {b / measured:.4f}")
+    for op in sorted(res):
+        e = res[op]
+        n = max(e["launches"], 1)
+        lines.append(f"op {op} launches {e['launches']} fetch_bytes_per_launch {e['FETCH_SIZE'] / n:.0f} "
+                     f"write_bytes_per_launch {e['WRITE_SIZE'] / n:.0f} "
+                     f"traffic_bytes_per_launch {(e['FETCH_SIZE'] + e['WRITE_SIZE']) / n:.0f}")
+    with open(TRAFFIC_FILE, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def load_traffic():
+    """op -> HBM bytes per launch, or {} when missing or taken on different kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            lines = fh.read().splitlines()
+    except OSError:
+        return {}
+    out, src = {}, None
+    for ln in lines:
+        f = ln.split()
+        if f and f[0] == "kernel_source_hash":
+            src = f[1]
+        elif f and f[0] == "op":
+            out[f[1]] = float(f[f.index("traffic_bytes_per_launch") + 1])
+    return out if src == kernel_source_hash() else {}
 
 
 def log(*a):
@@ -116,7 +240,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=512)
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     args = ap.parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
               "(data-parallel ranks would each run this same step on their own tokens)", file=sys.stderr)
@@ -133,6 +261,13 @@ def main():
     log(f"  drawn in {time.time() - t0:.1f} s")
     ops, keep = build_step(P, torch, d)
     stream = torch.cuda.current_stream()
+
+    # calibration copy for the HBM-traffic counters (untimed; reads and writes COPY_BYTES)
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
 
     def step(events=None):
         for i, (_, fn, _, _) in enumerate(ops):
@@ -170,6 +305,7 @@ def main():
             e["flops"] += work.get("flops", 0)
             e["bytes"] += work.get("bytes", 0)
     kernels = {}
+    hbm = load_traffic()
     for name, e in per.items():
         tot = sum(e["ms"])
         avg = tot / len(e["ms"])
@@ -181,22 +317,26 @@ def main():
         else:
             gbs = e["bytes"] / (tot / 1e3) / 1e9
             row.update({"GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)})
+        row["alg_bytes_per_launch"] = e["bytes"] // e["launches"]
+        row["hbm_bytes_per_launch"] = round(hbm[name]) if name in hbm else None
         kernels[name] = row
 
     gemm_flops = sum(w.get("flops", 0) for _, _, w, _ in ops)
     value = gemm_flops / (ms_per_step / 1e3) / 1e12
     dom = max(per, key=lambda n: sum(per[n]["ms"]))
     de = per[dom]
+    traffic = load_traffic().get(dom)
+    traffic = None if traffic is None else round(traffic)
     avg_ms = sum(de["ms"]) / len(de["ms"])
     if de["kind"] == "gemm":
         achieved = (de["flops"] / de["launches"]) / (avg_ms / 1e3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / FP8_PEAK_TFLOPS, 4), "traffic": None, "kernel": dom,
+                "frac": round(achieved / FP8_PEAK_TFLOPS, 4), "traffic": traffic, "kernel": dom,
                 "avg_launch_us": round(1000 * avg_ms, 2)}
     else:
         achieved = (de["bytes"] / de["launches"]) / (avg_ms / 1e3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": dom,
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": dom,
                 "avg_launch_us": round(1000 * avg_ms, 2)}
 
     cpu = None
