@@ -211,8 +211,9 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
   const int fcol[4] = {((4 * h + 0) ^ fsw) << 4, ((4 * h + 1) ^ fsw) << 4, ((4 * h + 2) ^ fsw) << 4,
                        ((4 * h + 3) ^ fsw) << 4};
 
-  // FWD/DGRAD: product of the last tile of a slice, promoted by the next slice's block
-  v16f pcarry = zero;
+  // product of the last tile of a slice, promoted by the next slice's block (WGRAD: together
+  // with the column scales of the last column tile)
+  v16f pcarry = zero, sbcarry = zero;
   float scp = 0.0f;
 
   issue_slice(kb_begin, 0);
@@ -221,33 +222,27 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
 
   for (int kb = kb_begin; kb < kb_end; ++kb) {
     const int stage = (kb - kb_begin) & 1;
-    // (FWD/DGRAD: the operand copy of the next slice is issued inside the asm block)
-    if (MODE == 2 && kb + 1 < kb_end) issue_slice(kb + 1, stage ^ 1);
     const uint8_t* st = smem + stage * kStageBytes;
-    const uint8_t* As = st + (wm * 64 + l32) * kBK;
-    const uint8_t* Bs = st + kStageA + (wn * 128 + l32) * kBK;
     const float* sAs = reinterpret_cast<const float*>(st + kStageA + kStageB);
     const float* sBs = reinterpret_cast<const float*>(st + kStageA + kStageB + 1024);
 
-    // FWD/DGRAD: the wave's 128 columns lie in one 128-column weight block (index wn)
+    // row scales of the lane's two rows; FWD/DGRAD fold in the 128x128 weight-block scale
+    // (the wave's 128 columns lie in one block, index wn)
     const float sbb = (MODE != 2) ? sBs[wn] : 1.0f;
-    float sc[2];
-#pragma unroll
-    for (int mi = 0; mi < 2; ++mi) sc[mi] = sAs[wm * 64 + mi * 32 + l32] * sbb;
+    const float sc0 = sAs[wm * 64 + l32] * sbb, sc1 = sAs[wm * 64 + 32 + l32] * sbb;
 
+    // LDS byte addresses of this lane's four swizzled 16-byte chunks in its A row and in its B
+    // row of the current stage
+    const uint32_t sbase = lds_addr(st);
+    const uint32_t arow = sbase + (uint32_t)((wm * 64 + l32) * kBK);
+    const uint32_t brow = sbase + (uint32_t)(kStageA + (wn * 128 + l32) * kBK);
+    // next slice (the last slice re-copies itself into the idle stage, so the block has no
+    // branch); its scales are copied here, after this slice's scales were read
+    const int kn = kb + 1 < kb_end ? kb + 1 : kb;
+    if (kb + 1 < kb_end) issue_scales(kb + 1, stage ^ 1);
+    const int64_t ko = (int64_t)kn * kBK;
+    const uint32_t m0 = lds_addr(smem + (stage ^ 1) * kStageBytes) + (uint32_t)(wave * 32 * kBK);
     if constexpr (MODE != 2) {
-      // hand-scheduled slice (gemm_slice_asm.inc): LDS byte addresses of this lane's four
-      // swizzled 16-byte chunks in its A row and in its B row of the current stage
-      const uint32_t sbase = lds_addr(st);
-      const uint32_t arow = sbase + (uint32_t)((wm * 64 + l32) * kBK);
-      const uint32_t brow = sbase + (uint32_t)(kStageA + (wn * 128 + l32) * kBK);
-      const float sc0 = sc[0], sc1 = sc[1];
-      // next slice (the last slice re-copies itself into the idle stage, so the block has
-      // no branch); its scales are copied here, after this slice's scales were read
-      const int kn = kb + 1 < kb_end ? kb + 1 : kb;
-      if (kb + 1 < kb_end) issue_scales(kb + 1, stage ^ 1);
-      const int64_t ko = (int64_t)kn * kBK;
-      const uint32_t m0 = lds_addr(smem + (stage ^ 1) * kStageBytes) + (uint32_t)(wave * 32 * kBK);
       asm volatile(PURO_SLICE_ASM_ROWSCALE
                    : "+{v[0:15]}"(acc[0]), "+{v[16:31]}"(acc[1]), "+{v[32:47]}"(acc[2]), "+{v[48:63]}"(acc[3]),
                      "+{v[64:79]}"(acc[4]), "+{v[80:95]}"(acc[5]), "+{v[96:111]}"(acc[6]), "+{v[112:127]}"(acc[7]),
@@ -261,74 +256,32 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
                      [gb2] "s"(b_grp[2] + ko), [gb3] "s"(b_grp[3] + ko), [oa0] "v"(a_off[0]), [oa1] "v"(a_off[1]),
                      [ob0] "v"(b_off[0]), [ob1] "v"(b_off[1]), [m0] "s"(m0)
                    : PURO_SLICE_ASM_CLOBBERS, "m0", "memory");
-      scp = sc1;  // tile 7's product stays in pcarry until the next block (or the tail)
-      continue;   // the block ended with the slice's wait and barrier
     } else {
-      auto frag = [&](const uint8_t* rowp, v8i& f0, v8i& f1) {
-        g_u32x4 c[4];
-  #pragma unroll
-        for (int j = 0; j < 4; ++j) c[j] = *reinterpret_cast<const g_u32x4*>(rowp + fcol[j]);
-        f0 = join(c[0], c[1]);
-        f1 = join(c[2], c[3]);
-      };
-      v8i af[2][2];
-  #pragma unroll
-      for (int mi = 0; mi < 2; ++mi) frag(As + mi * 32 * kBK, af[mi][0], af[mi][1]);
-
-      // 8 MFMA tiles per slice (column-tile major), software-pipelined.  Step s issues, in
-      // this order: half of the next column tile's B-fragment reads (prefetch), the two MFMAs
-      // of tile s, and the 16 promotion FMAs of tile s-1.  Every LDS wait then covers reads
-      // issued a full step earlier.  (WGRAD reads its 16 column scales per tile instead of
-      // prefetching, to stay within 256 VGPRs.)
-      constexpr bool kPrefetchB = MODE != 2;
-      v8i bc[2], bn[2];
-      frag(Bs, bc[0], bc[1]);
-      g_u32x4 nc[4];
-      v16f pr[2];
-  #pragma unroll
-      for (int s = 0; s <= 8; ++s) {
-        if (s < 8) {
-          const int ni = s >> 1, mi = s & 1;
-          if (kPrefetchB && ni < 3) {
-            const uint8_t* rowp = Bs + (ni + 1) * 32 * kBK;
-            nc[2 * mi + 0] = *reinterpret_cast<const g_u32x4*>(rowp + fcol[2 * mi + 0]);
-            nc[2 * mi + 1] = *reinterpret_cast<const g_u32x4*>(rowp + fcol[2 * mi + 1]);
-          }
-          if (!kPrefetchB && mi == 0 && ni > 0) frag(Bs + ni * 32 * kBK, bc[0], bc[1]);
-          pr[s & 1] = mfma_32x32x64_e4m3(bc[0], af[mi][0], zero);
-          pr[s & 1] = mfma_32x32x64_e4m3(bc[1], af[mi][1], pr[s & 1]);
-          if (kPrefetchB && mi == 1 && ni < 3) {
-            bc[0] = join(nc[0], nc[1]);
-            bc[1] = join(nc[2], nc[3]);
-          }
-        }
-        if (s > 0) {
-          const int q = s - 1, ni = q >> 1, mi = q & 1;
-          const v16f& pq = pr[q & 1];
-          if (MODE != 2) {
-  #pragma unroll
-            for (int v = 0; v < 16; ++v) acc[2 * ni + mi][v] = __builtin_fmaf(pq[v], sc[mi], acc[2 * ni + mi][v]);
-          } else {
-            const float* sbp = sBs + wn * 128 + ni * 32 + 4 * h;
-  #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              const g_f32x4 sbw = *reinterpret_cast<const g_f32x4*>(sbp + 8 * g);
-  #pragma unroll
-              for (int e = 0; e < 4; ++e)
-                acc[2 * ni + mi][4 * g + e] = __builtin_fmaf(pq[4 * g + e], sc[mi] * sbw[e], acc[2 * ni + mi][4 * g + e]);
-            }
-          }
-        }
-        // hard fence: nothing moves across steps, so prefetch reads stay one step ahead
-        __builtin_amdgcn_sched_barrier(0);
-      }
+      // the lane's column scales: columns wn*128 + ni*32 + 8g + 4h .. +3 (ni, g immediates)
+      const uint32_t sbj = sbase + (uint32_t)(kStageA + kStageB + 1024 + (wn * 128 + 4 * h) * 4);
+      asm volatile(PURO_SLICE_ASM_COLSCALE
+                   : "+{v[0:15]}"(acc[0]), "+{v[16:31]}"(acc[1]), "+{v[32:47]}"(acc[2]), "+{v[48:63]}"(acc[3]),
+                     "+{v[64:79]}"(acc[4]), "+{v[80:95]}"(acc[5]), "+{v[96:111]}"(acc[6]), "+{v[112:127]}"(acc[7]),
+                     "+{v[144:159]}"(pcarry), "+{v[208:223]}"(sbcarry)
+                   : [aj0] "v"(arow + fcol[0]), [aj1] "v"(arow + fcol[1]), [aj2] "v"(arow + fcol[2]),
+                     [aj3] "v"(arow + fcol[3]), [bj0] "v"(brow + fcol[0]), [bj1] "v"(brow + fcol[1]),
+                     [bj2] "v"(brow + fcol[2]), [bj3] "v"(brow + fcol[3]), [sa0] "v"(sc0), [sa1] "v"(sc1),
+                     [sap] "v"(scp), [sbj] "v"(sbj),
+                     [ga0] "s"(a_grp[0] + ko), [ga1] "s"(a_grp[1] + ko), [ga2] "s"(a_grp[2] + ko),
+                     [ga3] "s"(a_grp[3] + ko), [gb0] "s"(b_grp[0] + ko), [gb1] "s"(b_grp[1] + ko),
+                     [gb2] "s"(b_grp[2] + ko), [gb3] "s"(b_grp[3] + ko), [oa0] "v"(a_off[0]), [oa1] "v"(a_off[1]),
+                     [ob0] "v"(b_off[0]), [ob1] "v"(b_off[1]), [m0] "s"(m0)
+                   : PURO_SLICE_ASM_COLSCALE_CLOBBERS, "m0", "memory");
     }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    scp = sc1;  // tile 7's product stays in pcarry until the next block (or the tail)
+    // (the block ended with the slice's wait and barrier)
   }
 
   if constexpr (MODE != 2)
     asm volatile(PURO_SLICE_ASM_ROWSCALE_TAIL : "+{v[112:127]}"(acc[7]) : "{v[144:159]}"(pcarry), [scp] "v"(scp));
+  else
+    asm volatile(PURO_SLICE_ASM_COLSCALE_TAIL : "+{v[112:127]}"(acc[7]), "+{v[144:159]}"(pcarry)
+                 : "{v[208:223]}"(sbcarry), [sap] "v"(scp));
 
   // ---- epilogue through LDS (free after the loop's last barrier): each wave stages its own
   // output tile, one 32-row half at a time, in a private LDS region with a padded row stride

@@ -1,9 +1,17 @@
-"""Generate gemm_slice_asm.inc: the hand-scheduled gfx950 instruction sequence for one
-128-deep slice of the blockwise-scaled FP8 GEMM (FWD / DGRAD, row-scale promotion).
+"""Generate gemm_slice_asm.inc: the hand-scheduled gfx950 instruction sequences for one
+128-deep slice of the blockwise-scaled FP8 GEMM.
 
     python blockwise_scaled_fp8_quant_amd/csrc/gen_slice_asm.py   # rewrites gemm_slice_asm.inc
 
 The generated text is committed; the library build does not run this script.
+
+Two variants, differing in how the slice product of a tile is promoted:
+  ROWSCALE (FWD / DGRAD)  one scale per lane and row group: sA(i,kb) * sB(block,kb) is the
+                          same for the 16 columns a lane owns (they sit in one 128x128
+                          weight block), so the promotion is 16 FMAs:  C += P * sc.
+  COLSCALE (WGRAD)        sB(j,kb) differs per column: 16 multiplies by the lane's 16 column
+                          scales (read from LDS) and 16 FMAs by its row scale:
+                          P *= sB(j);  C += P * sA(i).
 
 Register map (per lane; pinned by the asm statement's constraints and clobbers):
   v[0:127]    accumulators: output tile T = 2*ni + mi (32 x 32, 16 fp32 per lane) in v[16T:16T+15]
@@ -12,131 +20,228 @@ Register map (per lane; pinned by the asm statement's constraints and clobbers):
               promoted at the start of the next block (or by the tail block after the loop)
   v[160:175]  A fragment, row group mi = 0 (4 x 16-byte LDS chunks per lane)
   v[176:191]  A fragment, row group mi = 1
-  v[192:207]  B fragment buffer 0 (column tiles ni = 0, 2), v[208:223] buffer 1 (ni = 1, 3)
+  ROWSCALE:   v[192:207] B fragment buffer 0 (column tiles ni = 0, 2), v[208:223] buffer 1 (ni = 1, 3)
+  COLSCALE:   v[192:207] B fragment (one buffer), v[208:223] the 16 column scales of the current
+              column tile (column tile 3's are carried out of the block with tile 7's product)
 Operands: %[aj0..3] / %[bj0..3] LDS byte addresses of this lane's 4 swizzled 16-byte chunks in
-its A / B row (row group / column tile offsets are 4096-byte immediates); %[sc0], %[sc1] the
-promotion scale of row group 0 / 1 for this slice; %[scp] the scale of the carried product;
-for the copy of the next slice into the other LDS stage: %[ga0..3] / %[gb0..3] the
-(wave-uniform) global addresses of the wave's four 8-row groups of A / B at that slice,
-%[oa0], %[oa1] / %[ob0], %[ob1] the lane's byte offset within an even / odd group (row in
-group and swizzled chunk), %[m0] the LDS address of the wave's first A row in the other stage.
+its A / B row (row group / column tile offsets are 4096-byte immediates); ROWSCALE: %[sc0],
+%[sc1] the promotion scale of row group 0 / 1 for this slice, %[scp] the scale of the carried
+product; COLSCALE: %[sa0], %[sa1], %[sap] the row scales likewise and %[sbj] the LDS address
+of the lane's first column-scale quad (column tile / quad offsets are immediates); for the copy
+of the next slice into the other LDS stage: %[ga0..3] / %[gb0..3] the (wave-uniform) global
+addresses of the wave's four 8-row groups of A / B at that slice, %[oa0], %[oa1] / %[ob0],
+%[ob1] the lane's byte offset within an even / odd group (row in group and swizzled chunk),
+%[m0] the LDS address of the wave's first A row in the other stage.
 
-Schedule:
-  entry   read the first B fragment and the A fragment of row group 0; pad; promote the
-          carried tile-7 product of the previous slice; read the A fragment of row group 1;
-          wait for the first eight reads only.
-  step s  (s = 0..7, tile (ni, mi) = (s >> 1, s & 1)):
-          1. wait for this step's fragments (the B fragment read two steps earlier, or A of
-             row group 1), counting only the older reads;
-          2. the two chained MFMAs of tile s, back to back (the second accumulates on the
-             first: v_mfma_f32_32x32x64_f8f6f4, one 128-deep slice of a 32 x 32 tile);
-          3. one of the eight global_load_lds_dwordx4 copies of the next slice (M0 = LDS
-             destination, one wait state after the M0 write): spreading the copies over the
-             slice keeps the address unit's queue from stalling the wave;
-          4. on mi == 0, the four LDS reads of the next column tile's B fragment (into the
-             other buffer, last read by the MFMAs two instructions earlier);
-          5. padding so that at least 20 wait states separate the MFMA that produced tile
-             s-1's product from its first VALU read (the spacing the compiler's own hazard
-             recognizer uses for 16-pass XDL results on gfx950);
-          6. the 16 promotion FMAs of tile s-1:  C_acc += P * sc.
+Schedule of a slice (8 steps, step s computes tile (ni, mi) = (s >> 1, s & 1)):
+  entry   read the first B fragment and the A fragment of row group 0; promote the carried
+          tile-7 product of the previous slice; read the A fragment of row group 1.
+  step s  wait for this step's fragments (counting only older LDS reads); the two chained
+          MFMAs of tile s (v_mfma_f32_32x32x64_f8f6f4: the second accumulates on the first,
+          together one 128-deep slice of a 32 x 32 tile); one of the eight
+          global_load_lds_dwordx4 copies of the next slice (M0 = LDS destination, one wait
+          state after the M0 write; spreading the copies over the slice keeps the address
+          unit's queue from stalling the wave); fragment / scale reads for later steps; the
+          promotion of tile s-1.
   exit    wait for this wave's copies, then meet the other waves at the barrier.
 Every LDS read is waited for inside the block.
+
+Hazards: a VALU read of an MFMA result needs HAZARD_WAIT_STATES wait states (instructions, or
+s_nop k = k + 1) after the MFMA was issued (the figure the compiler's own hazard recognizer
+uses for 16-pass XDL results on gfx950).  The generator counts the instructions between
+each product's last MFMA and its first VALU read and pads only where they fall short.
+Fragment registers are overwritten by LDS reads only after the MFMAs reading them were
+issued (MFMAs read their A/B operands when they issue).
 """
 import os
 
 HAZARD_WAIT_STATES = 20
+STAGE_B = 32768                      # byte offset of the B tile in an LDS stage
+P_EVEN, P_ODD = 128, 144
+A0, A1, BF0, SB = 160, 176, 192, 208
 
 
-def nops(n):
-    out = []
-    while n > 0:
-        k = min(n, 16)
-        out.append(f"s_nop {k - 1}")
-        n -= k
-    return out
+class Emitter:
+    """Collects instructions, counts wait states, and checks the LDS-read bookkeeping: every
+    register an MFMA or VALU instruction reads must not be the target of an LDS read that no
+    s_waitcnt has covered yet (LDS reads return in order, so lgkmcnt(n) covers all but the
+    newest n)."""
+
+    def __init__(self):
+        self.lines = []
+        self.ws = 0                  # wait states issued so far
+        self.produced = {}           # P buffer -> wait-state count just after its last MFMA
+        self.pending = []            # register sets of LDS reads not yet waited for, oldest first
+
+    def emit(self, ln):
+        self.lines.append(ln)
+        self.ws += int(ln.split()[1]) + 1 if ln.startswith("s_nop") else 1
+
+    def nops(self, n):
+        while n > 0:
+            k = min(n, 16)
+            self.emit(f"s_nop {k - 1}")
+            n -= k
+
+    def wait_lgkm(self, n):
+        self.emit(f"s_waitcnt lgkmcnt({n})")
+        self.pending = self.pending[len(self.pending) - n:] if n else []
+
+    def use(self, regs):
+        for p in self.pending:
+            assert not (p & regs), f"register read before its LDS read was waited for: {sorted(p & regs)[:4]}"
+
+    def read(self, dst, addr, offset):
+        regs = set(range(dst, dst + 4))
+        for p in self.pending:
+            assert not (p & regs), "LDS read overwrites registers of a pending read"
+        self.emit(f"ds_read_b128 v[{dst}:{dst + 3}], %[{addr}] offset:{offset}")
+        self.pending.append(regs)
+        assert len(self.pending) <= 15, "more LDS reads in flight than lgkmcnt can count"
+
+    def frag(self, dst, addr, offset):
+        """4 LDS reads: the lane's 4 swizzled 16-byte chunks of one A / B fragment."""
+        for j in range(4):
+            self.read(dst + 4 * j, f"{addr}{j}", offset)
+
+    def mfma_pair(self, p, b, a):
+        self.use(set(range(b, b + 16)) | set(range(a, a + 16)))
+        self.emit(f"v_mfma_f32_32x32x64_f8f6f4 v[{p}:{p + 15}], v[{b}:{b + 7}], v[{a}:{a + 7}], 0")
+        self.emit(f"v_mfma_f32_32x32x64_f8f6f4 v[{p}:{p + 15}], v[{b + 8}:{b + 15}], v[{a + 8}:{a + 15}], v[{p}:{p + 15}]")
+        self.produced[p] = self.ws
+
+    def hazard(self, p):
+        """Pad before the first VALU read of product buffer p (produced in this block)."""
+        self.nops(HAZARD_WAIT_STATES - (self.ws - self.produced[p]))
+
+    def dma(self, k):
+        """Copy k of the next slice: group q = k >> 1, A for even k, B for odd k."""
+        q = k >> 1
+        if k & 1 == 0:
+            self.emit(f"s_add_u32 m0, %[m0], {q * 8 * 128}")
+            self.emit("s_nop 0")
+            self.emit(f"global_load_lds_dwordx4 %[oa{q & 1}], %[ga{q}]")
+        else:
+            self.emit(f"s_add_u32 m0, %[m0], {STAGE_B + q * 8 * 128}")
+            self.emit("s_nop 0")
+            self.emit(f"global_load_lds_dwordx4 %[ob{q & 1}], %[gb{q}]")
+
+    def fma_row(self, T, p, sc):
+        for v in range(16):
+            self.emit(f"v_fmac_f32 v{16 * T + v}, v{p + v}, %[{sc}]")
+
+    def fma_col(self, T, p, sa):
+        self.use(set(range(SB, SB + 16)))
+        for v in range(16):
+            self.emit(f"v_mul_f32 v{p + v}, v{p + v}, v{SB + v}")
+        for v in range(16):
+            self.emit(f"v_fmac_f32 v{16 * T + v}, v{p + v}, %[{sa}]")
+
+    def sb_reads(self, ni):
+        """The lane's 16 column scales of column tile ni: 4 quads (columns 8g + 4h .. +3)."""
+        for g in range(4):
+            self.read(SB + 4 * g, "sbj", ni * 128 + 32 * g)
 
 
-def dma(k):
-    """Copy k of the next slice: group q = k >> 1, A for even k, B for odd k."""
-    q = k >> 1
-    if k & 1 == 0:
-        return [f"s_add_u32 m0, %[m0], {q * 8 * 128}", "s_nop 0",
-                f"global_load_lds_dwordx4 %[oa{q & 1}], %[ga{q}]"]
-    return [f"s_add_u32 m0, %[m0], {32768 + q * 8 * 128}", "s_nop 0",
-            f"global_load_lds_dwordx4 %[ob{q & 1}], %[gb{q}]"]
-
-
-def reads(dst, addr, offset):
-    return [f"ds_read_b128 v[{dst + 4 * j}:{dst + 4 * j + 3}], %[{addr}{j}] offset:{offset}" for j in range(4)]
-
-
-def fmas(T, p, sc):
-    return [f"v_fmac_f32 v{16 * T + v}, v{p + v}, %[{sc}]" for v in range(16)]
-
-
-def waits(n_instr):
-    """Wait states an instruction list contributes (s_nop k counts k + 1)."""
-    return n_instr
-
-
-def generate():
-    L = []
-    # entry
-    L += reads(192, "bj", 0)            # B, column tile 0 -> buffer 0
-    L += reads(160, "aj", 0)            # A, row group 0
-    L += nops(HAZARD_WAIT_STATES - 8)   # carried product came from the previous block's last MFMA
-    L += fmas(7, 144, "scp")
-    L += reads(176, "aj", 4096)         # A, row group 1
-    L.append("s_waitcnt lgkmcnt(4)")
+def gen_rowscale():
+    e = Emitter()
+    e.frag(BF0, "bj", 0)                  # B, column tile 0 -> buffer 0
+    e.frag(A0, "aj", 0)                   # A, row group 0
+    e.nops(HAZARD_WAIT_STATES - 8)        # carried product: counted from the block start
+    e.fma_row(7, P_ODD, "scp")
+    e.frag(A1, "aj", 4096)                # A, row group 1
+    e.wait_lgkm(4)                        # B(0), A0
     for s in range(8):
         ni, mi = s >> 1, s & 1
-        bb = 192 + 16 * (ni & 1)
-        ab = 160 + 16 * mi
-        p = 128 + 16 * (s & 1)
         if s == 1:
-            L.append("s_waitcnt lgkmcnt(4)")          # A row group 1 (B of tile 1 is newer)
+            e.wait_lgkm(4)                # A1 (the B fragment of tile 2 is newer)
         elif mi == 0 and ni > 0:
-            L.append("s_waitcnt lgkmcnt(0)")          # B fragment read two steps earlier
-        L.append(f"v_mfma_f32_32x32x64_f8f6f4 v[{p}:{p + 15}], v[{bb}:{bb + 7}], v[{ab}:{ab + 7}], 0")
-        L.append(f"v_mfma_f32_32x32x64_f8f6f4 v[{p}:{p + 15}], v[{bb + 8}:{bb + 15}], v[{ab + 8}:{ab + 15}], v[{p}:{p + 15}]")
-        ws = 2
-        d = dma(s)
-        L += d
-        ws += 3 + 0                                    # s_add, s_nop 0 (1 wait state), load
+            e.wait_lgkm(0)                # B fragment read two steps earlier
+        e.mfma_pair(P_EVEN if mi == 0 else P_ODD, BF0 + 16 * (ni & 1), A0 + 16 * mi)
+        e.dma(s)
         if mi == 0 and ni < 3:
-            L += reads(192 + 16 * ((ni + 1) & 1), "bj", (ni + 1) * 4096)
-            ws += 4
+            e.frag(BF0 + 16 * ((ni + 1) & 1), "bj", (ni + 1) * 4096)
         if s > 0:
-            L += nops(HAZARD_WAIT_STATES - ws)
             q = s - 1
-            L += fmas(2 * (q >> 1) + (q & 1), 128 + 16 * (q & 1), f"sc{q & 1}")
-    L.append("s_waitcnt vmcnt(0) lgkmcnt(0)")
-    L.append("s_barrier")
-    return L
+            pq = P_EVEN if (q & 1) == 0 else P_ODD
+            e.hazard(pq)
+            e.fma_row(2 * (q >> 1) + (q & 1), pq, f"sc{q & 1}")
+    e.emit("s_waitcnt vmcnt(0) lgkmcnt(0)")
+    e.emit("s_barrier")
+    return e.lines
 
 
-def generate_tail():
-    """After the last slice: promote the carried tile-7 product."""
-    return nops(HAZARD_WAIT_STATES) + fmas(7, 144, "scp")
+def gen_colscale():
+    e = Emitter()
+    e.frag(BF0, "bj", 0)                  # B, column tile 0
+    e.frag(A0, "aj", 0)                   # A, row group 0
+    e.nops(HAZARD_WAIT_STATES - 8)        # carried product: counted from the block start
+    e.fma_col(7, P_ODD, "sap")            # the previous slice's column-tile-3 scales
+    e.frag(A1, "aj", 4096)                # A, row group 1
+    e.wait_lgkm(4)                        # B(0), A0
+    for s in range(8):
+        ni, mi = s >> 1, s & 1
+        if s == 1:
+            e.wait_lgkm(4)                # A1 (the scales of column tile 0 are newer)
+        elif mi == 0 and ni > 0:
+            e.wait_lgkm(0)                # B(ni), read at the previous step
+        e.mfma_pair(P_EVEN if mi == 0 else P_ODD, BF0, A0 + 16 * mi)
+        e.dma(s)
+        if mi == 1 and ni < 3:
+            e.frag(BF0, "bj", (ni + 1) * 4096)   # B(ni+1): the MFMAs reading B(ni) have issued
+        if s == 0:
+            e.sb_reads(0)
+        if s > 0:
+            q = s - 1
+            pq = P_EVEN if (q & 1) == 0 else P_ODD
+            if mi == 1:                   # tile (ni, 0): column tile ni's scales (older than B(ni+1))
+                e.wait_lgkm(4 if ni < 3 else 0)
+            e.hazard(pq)
+            e.fma_col(2 * (q >> 1) + (q & 1), pq, f"sa{q & 1}")
+            if mi == 0:                   # tile (ni-1, 1) was the last user of the old scales
+                e.sb_reads(ni)
+    e.emit("s_waitcnt vmcnt(0) lgkmcnt(0)")
+    e.emit("s_barrier")
+    assert not e.pending
+    return e.lines
+
+
+def gen_tail(col):
+    """After the last slice: promote the carried tile-7 product (padding kept for a block
+    boundary the generator cannot see)."""
+    e = Emitter()
+    e.nops(HAZARD_WAIT_STATES)
+    if col:
+        e.fma_col(7, P_ODD, "sap")
+    else:
+        e.fma_row(7, P_ODD, "scp")
+    return e.lines
+
+
+def macro(name, lines):
+    out = [f"#define {name} \\"]
+    out += [f'  "{ln}\\n\\t" \\' for ln in lines]
+    out.append('  ""')
+    return "\n".join(out) + "\n"
 
 
 def main():
-    lines = generate()
+    row, col = gen_rowscale(), gen_colscale()
     here = os.path.dirname(os.path.abspath(__file__))
     with open(os.path.join(here, "gemm_slice_asm.inc"), "w") as f:
-        f.write("// Generated by gen_slice_asm.py -- one 128-deep slice of the FWD/DGRAD GEMM (see there).\n")
-        f.write("#define PURO_SLICE_ASM_ROWSCALE \\\n")
-        for ln in lines:
-            f.write(f'  "{ln}\\n\\t" \\\n')
-        f.write('  ""\n')
+        f.write("// Generated by gen_slice_asm.py -- one 128-deep slice of the FP8 GEMM (see there).\n")
+        f.write("// FWD / DGRAD: one promotion scale per lane and row group\n")
+        f.write(macro("PURO_SLICE_ASM_ROWSCALE", row))
         f.write("// promotion of the carried product after the last slice\n")
-        f.write("#define PURO_SLICE_ASM_ROWSCALE_TAIL \\\n")
-        for ln in generate_tail():
-            f.write(f'  "{ln}\\n\\t" \\\n')
-        f.write('  ""\n')
-        f.write("// VGPRs the block uses besides the pinned accumulators and the carried product\n")
+        f.write(macro("PURO_SLICE_ASM_ROWSCALE_TAIL", gen_tail(False)))
+        f.write("// WGRAD: per-column scales from LDS times one row scale per lane and row group\n")
+        f.write(macro("PURO_SLICE_ASM_COLSCALE", col))
+        f.write(macro("PURO_SLICE_ASM_COLSCALE_TAIL", gen_tail(True)))
+        f.write("// VGPRs the blocks use besides the pinned accumulators and the carried product (and, for\n"
+                "// COLSCALE, the carried column scales in v[208:223])\n")
         f.write("#define PURO_SLICE_ASM_CLOBBERS " + ", ".join(f'"v{r}"' for r in list(range(128, 144)) + list(range(160, 224))) + "\n")
-    print(f"{len(lines)} instructions")
+        f.write("#define PURO_SLICE_ASM_COLSCALE_CLOBBERS " + ", ".join(f'"v{r}"' for r in list(range(128, 144)) + list(range(160, 208))) + "\n")
+    print(f"rowscale {len(row)} instructions, colscale {len(col)} instructions")
 
 
 if __name__ == "__main__":
