@@ -3,13 +3,15 @@
 One step = one pass of the whole path over the full-layer workload at 16384 tokens
 (4 sequences of 4096), seed 0: for each of the 4 linear weights of one ~2B-scale layer
 (qkv 4096x2048, o 2048x2048, gate+up 12288x2048, down 2048x6144):
-    quantize W 128x128 (+ transposed copy), X 1x128, dY 1x128, dY 128x1, X 128x1;
-    FWD   Y  = X  W^T   (bf16 out)
-    DGRAD dX = dY W     (bf16 out)
-    WGRAD dW = dY^T X   (fp32 out)
+    quantize W 128x128 (+ transposed copy);
+    quantize X  1x128 and 128x1 in one pass (dual quantizer);  FWD   Y  = X  W^T  (bf16 out)
+    quantize dY 1x128 and 128x1 in one pass (dual quantizer);  DGRAD dX = dY W    (bf16 out)
+                                                                WGRAD dW = dY^T X  (fp32 out)
 Inputs are seeded synthetic bf16 tensors already resident in HBM when timing starts.
 Prints ONE JSON line.  `value` = GEMM TFLOP/s of the whole step (all 12 GEMMs' flops
-divided by the step time, quantizers included in the time).
+divided by the step time, quantizers included in the time).  After the timed steps the
+standalone 1x128 and 128x1 quantizers are timed on the same tensors (reported under
+`kernels` with "in_step": false; not part of `value`).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
 
@@ -68,6 +70,8 @@ def op_of_kernel(name: str, last_gemm):
         return "gemm_wgrad"
     if "split_reduce" in name or "zero_fill" in name:
         return last_gemm
+    if "quant_dual" in name:
+        return "quant_act_dual"
     if "quant_1x128" in name:
         return "quant_act_1x128"
     if "quant_128x128" in name:
@@ -160,10 +164,11 @@ def log(*a):
 
 
 def build_step(P, torch, d):
-    """Allocate every buffer once; return the list of (kernel name, launch thunk, work dict)."""
+    """Allocate every buffer once; return the step's (kernel name, launch thunk, work dict,
+    weight) list, the standalone single-quantizer list timed after the step, and the buffers."""
     from workloads import SWEEP_WEIGHTS
     dev = "cuda:0"
-    ops = []
+    ops, single = [], []
 
     def bf16(b):
         import numpy as np
@@ -185,19 +190,24 @@ def build_step(P, torch, d):
         dW = f32(dout, din)
         keep += [X, W, dY, Wq, Ws, WqT, WsT, Xq, Xs, Gq, Gs, GqT, GsT, XqT, XsT, Y, dX, dW]
         qb = lambda n: {"kind": "quant", "bytes": 2 * n + n + 4 * (n // 128)}
+        qdb = lambda n: {"kind": "quant", "bytes": 2 * n + 2 * n + 2 * 4 * (n // 128)}
         qwb = {"kind": "quant", "bytes": 2 * dout * din + 2 * dout * din + 2 * 4 * (dout // 128) * (din // 128)}
         gf = lambda m, n, k, ob: {"kind": "gemm", "flops": 2 * m * n * k, "bytes": m * k + n * k + 4 * (m + n) * (k // 128) + ob * m * n}
         ops += [
             ("quant_w_128x128", lambda W=W, Wq=Wq, Ws=Ws, WqT=WqT, WsT=WsT: P.puro_fp8_quant_w_128x128(W, Wq, Ws, WqT, WsT), qwb, wname),
-            ("quant_act_1x128", lambda X=X, Xq=Xq, Xs=Xs: P.puro_fp8_quant_act_1x128(X, Xq, Xs), qb(T * din), wname),
+            ("quant_act_dual", lambda X=X, Xq=Xq, Xs=Xs, XqT=XqT, XsT=XsT: P.puro_fp8_quant_act_dual(X, Xq, Xs, XqT, XsT), qdb(T * din), wname),
             ("gemm_fwd", lambda Xq=Xq, Xs=Xs, Wq=Wq, Ws=Ws, Y=Y: P.puro_fp8_gemm(P.FWD, Xq, Xs, Wq, Ws, C=Y, out_dtype=P.OUT_BF16), gf(T, dout, din, 2), wname),
-            ("quant_act_1x128", lambda dY=dY, Gq=Gq, Gs=Gs: P.puro_fp8_quant_act_1x128(dY, Gq, Gs), qb(T * dout), wname),
+            ("quant_act_dual", lambda dY=dY, Gq=Gq, Gs=Gs, GqT=GqT, GsT=GsT: P.puro_fp8_quant_act_dual(dY, Gq, Gs, GqT, GsT), qdb(T * dout), wname),
             ("gemm_dgrad", lambda Gq=Gq, Gs=Gs, WqT=WqT, WsT=WsT, dX=dX: P.puro_fp8_gemm(P.DGRAD, Gq, Gs, WqT, WsT, C=dX, out_dtype=P.OUT_BF16), gf(T, din, dout, 2), wname),
-            ("quant_act_128x1", lambda dY=dY, GqT=GqT, GsT=GsT: P.puro_fp8_quant_act_128x1(dY, GqT, GsT), qb(T * dout), wname),
-            ("quant_act_128x1", lambda X=X, XqT=XqT, XsT=XsT: P.puro_fp8_quant_act_128x1(X, XqT, XsT), qb(T * din), wname),
             ("gemm_wgrad", lambda GqT=GqT, GsT=GsT, XqT=XqT, XsT=XsT, dW=dW: P.puro_fp8_gemm(P.WGRAD, GqT, GsT, XqT, XsT, C=dW, out_dtype=P.OUT_FP32), gf(dout, din, T, 4), wname),
         ]
-    return ops, keep
+        single += [
+            ("quant_act_1x128", lambda X=X, Xq=Xq, Xs=Xs: P.puro_fp8_quant_act_1x128(X, Xq, Xs), qb(T * din), wname),
+            ("quant_act_1x128", lambda dY=dY, Gq=Gq, Gs=Gs: P.puro_fp8_quant_act_1x128(dY, Gq, Gs), qb(T * dout), wname),
+            ("quant_act_128x1", lambda dY=dY, GqT=GqT, GsT=GsT: P.puro_fp8_quant_act_128x1(dY, GqT, GsT), qb(T * dout), wname),
+            ("quant_act_128x1", lambda X=X, XqT=XqT, XsT=XsT: P.puro_fp8_quant_act_128x1(X, XqT, XsT), qb(T * din), wname),
+        ]
+    return ops, single, keep
 
 
 def cpu_baseline(d, tokens: int):
@@ -259,7 +269,7 @@ def main():
     t0 = time.time()
     d = draw(WORKLOAD)
     log(f"  drawn in {time.time() - t0:.1f} s")
-    ops, keep = build_step(P, torch, d)
+    ops, single, keep = build_step(P, torch, d)
     stream = torch.cuda.current_stream()
 
     # calibration copy for the HBM-traffic counters (untimed; reads and writes COPY_BYTES)
@@ -269,63 +279,74 @@ def main():
     torch.cuda.synchronize()
     del src, dst
 
-    def step(events=None):
-        for i, (_, fn, _, _) in enumerate(ops):
+    def run(op_list, events=None):
+        for i, (_, fn, _, _) in enumerate(op_list):
             if events is not None:
                 events[i][0].record(stream)
             fn()
             if events is not None:
                 events[i][1].record(stream)
 
+    def timed(op_list, iters):
+        """HIP events around every op of `iters` passes; returns (total ms, per-op stats)."""
+        ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in op_list]
+              for _ in range(iters)]
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for k in range(iters):
+            run(op_list, ev[k])
+        stop.record(stream)
+        torch.cuda.synchronize()
+        per = {}
+        for k in range(iters):
+            for i, (name, _, work, _) in enumerate(op_list):
+                e = per.setdefault(name, {"ms": [], "flops": 0, "bytes": 0, "launches": 0, "kind": work["kind"]})
+                e["ms"].append(ev[k][i][0].elapsed_time(ev[k][i][1]))
+                e["launches"] += 1
+                e["flops"] += work.get("flops", 0)
+                e["bytes"] += work.get("bytes", 0)
+        return start.elapsed_time(stop), per
+
+    hbm = load_traffic()
+
+    def rows(per, total_ms, iters, in_step):
+        out = {}
+        for name, e in per.items():
+            tot = sum(e["ms"])
+            row = {"in_step": in_step, "launches_per_step": e["launches"] // iters,
+                   "avg_us": round(1000 * tot / len(e["ms"]), 2)}
+            if in_step:
+                row["share_of_step"] = round(tot / total_ms, 4)
+            if e["kind"] == "gemm":
+                tf = e["flops"] / (tot / 1e3) / 1e12
+                row.update({"TFLOP/s": round(tf, 1), "frac_fp8_peak": round(tf / FP8_PEAK_TFLOPS, 4)})
+            else:
+                gbs = e["bytes"] / (tot / 1e3) / 1e9
+                row.update({"GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)})
+            row["alg_bytes_per_launch"] = e["bytes"] // e["launches"]
+            row["hbm_bytes_per_launch"] = round(hbm[name]) if name in hbm else None
+            out[name] = row
+        return out
+
     for _ in range(args.warmup):
-        step()
+        run(ops)
     torch.cuda.synchronize()
     log(f"warmup done ({args.warmup} steps); timing {args.steps} steps")
-
-    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in ops]
-          for _ in range(args.steps)]
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    for k in range(args.steps):
-        step(ev[k])
-    stop.record(stream)
-    torch.cuda.synchronize()
-    total_ms = start.elapsed_time(stop)
+    total_ms, per = timed(ops, args.steps)
     ms_per_step = total_ms / args.steps
+    kernels = rows(per, total_ms, args.steps, True)
 
-    # per-kernel durations (HIP events on the launch stream, inside the timed region)
-    per = {}
-    for k in range(args.steps):
-        for i, (name, _, work, wname) in enumerate(ops):
-            dt = ev[k][i][0].elapsed_time(ev[k][i][1])
-            e = per.setdefault(name, {"ms": [], "flops": 0, "bytes": 0, "launches": 0, "kind": work["kind"]})
-            e["ms"].append(dt)
-            e["launches"] += 1
-            e["flops"] += work.get("flops", 0)
-            e["bytes"] += work.get("bytes", 0)
-    kernels = {}
-    hbm = load_traffic()
-    for name, e in per.items():
-        tot = sum(e["ms"])
-        avg = tot / len(e["ms"])
-        row = {"launches_per_step": e["launches"] // args.steps, "avg_us": round(1000 * avg, 2),
-               "share_of_step": round(tot / total_ms, 4)}
-        if e["kind"] == "gemm":
-            tf = e["flops"] / (tot / 1e3) / 1e12
-            row.update({"TFLOP/s": round(tf, 1), "frac_fp8_peak": round(tf / FP8_PEAK_TFLOPS, 4)})
-        else:
-            gbs = e["bytes"] / (tot / 1e3) / 1e9
-            row.update({"GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)})
-        row["alg_bytes_per_launch"] = e["bytes"] // e["launches"]
-        row["hbm_bytes_per_launch"] = round(hbm[name]) if name in hbm else None
-        kernels[name] = row
+    # standalone single quantizers on the same tensors (outside the step)
+    run(single)
+    single_ms, single_per = timed(single, args.steps)
+    kernels.update(rows(single_per, single_ms, args.steps, False))
 
     gemm_flops = sum(w.get("flops", 0) for _, _, w, _ in ops)
     value = gemm_flops / (ms_per_step / 1e3) / 1e12
     dom = max(per, key=lambda n: sum(per[n]["ms"]))
     de = per[dom]
-    traffic = load_traffic().get(dom)
+    traffic = hbm.get(dom)
     traffic = None if traffic is None else round(traffic)
     avg_ms = sum(de["ms"]) / len(de["ms"])
     if de["kind"] == "gemm":
@@ -351,7 +372,8 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "fp8e4m3xfp8e4m3->fp32", "data": "synthetic",
         "config": {"workload": "layer_sweep: 16384 tokens, seed 0, weights qkv 4096x2048, o 2048x2048, "
-                               "gate_up 12288x2048, down 2048x6144; fwd+dgrad+wgrad + 5 quantizations each",
+                               "gate_up 12288x2048, down 2048x6144; per weight: W 128x128 (+T), X and dY dual "
+                               "1x128+128x1 quantization, fwd+dgrad+wgrad",
                    "tokens": 16384, "gemm_gflop_per_step": round(gemm_flops / 1e9, 1),
                    "parallelism": "single GPU"},
         "roofline": roof, "cpu_baseline": cpu, "kernels": kernels,

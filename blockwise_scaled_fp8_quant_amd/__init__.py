@@ -15,8 +15,8 @@ from typing import Optional, Tuple
 
 __all__ = [
     "LIB_PATH", "lib", "PuroError", "FWD", "DGRAD", "WGRAD", "OUT_BF16", "OUT_FP32",
-    "puro_fp8_quant_act_1x128", "puro_fp8_quant_act_128x1", "puro_fp8_quant_w_128x128",
-    "puro_fp8_gemm", "puro_fp8_gemm_workspace_size", "puro_fp8_cast_e4m3",
+    "puro_fp8_quant_act_1x128", "puro_fp8_quant_act_128x1", "puro_fp8_quant_act_dual",
+    "puro_fp8_quant_w_128x128", "puro_fp8_gemm", "puro_fp8_gemm_workspace_size", "puro_fp8_cast_e4m3",
     "puro_fp8_strerror", "puro_fp8_version", "EXPORTED_SYMBOLS",
 ]
 
@@ -27,14 +27,14 @@ OUT_BF16, OUT_FP32 = 0, 1
 MODE_NAMES = {"FWD": FWD, "DGRAD": DGRAD, "WGRAD": WGRAD}
 
 EXPORTED_SYMBOLS = (
-    "puro_fp8_quant_act_1x128", "puro_fp8_quant_act_128x1", "puro_fp8_quant_w_128x128",
+    "puro_fp8_quant_act_1x128", "puro_fp8_quant_act_128x1", "puro_fp8_quant_act_dual", "puro_fp8_quant_w_128x128",
     "puro_fp8_gemm", "puro_fp8_gemm_workspace_size", "puro_fp8_cast_e4m3",
     "puro_fp8_strerror", "puro_fp8_version",
 )
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is missing: build it first (python -m blockwise_scaled_fp8_quant_amd.build "
+        f"{LIB_PATH} is missing: build it first (python blockwise_scaled_fp8_quant_amd/build.py "
         f"or __graft_entry__.build()); there is no non-HIP implementation")
 
 # torch ships its own HIP runtime (same SONAME, libamdhip64.so.7).  It must be loaded
@@ -61,6 +61,7 @@ if len(_hip_runtimes_mapped()) > 1:
 _i64, _p, _int, _sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
 lib.puro_fp8_quant_act_1x128.argtypes = [_p, _i64, _i64, _i64, _p, _i64, _p, _p]
 lib.puro_fp8_quant_act_128x1.argtypes = [_p, _i64, _i64, _i64, _p, _i64, _p, _p]
+lib.puro_fp8_quant_act_dual.argtypes = [_p, _i64, _i64, _i64, _p, _i64, _p, _p, _i64, _p, _p]
 lib.puro_fp8_quant_w_128x128.argtypes = [_p, _i64, _i64, _i64, _p, _i64, _p, _p, _i64, _p, _p]
 lib.puro_fp8_gemm.argtypes = [_int, _i64, _i64, _i64, _p, _i64, _p, _p, _i64, _p, _p, _i64, _int, _p, _sz, _p]
 lib.puro_fp8_gemm_workspace_size.argtypes = [_int, _i64, _i64, _i64]
@@ -136,6 +137,24 @@ def puro_fp8_quant_act_128x1(x, qT=None, sT=None, stream=None) -> Tuple[object, 
     _check(lib.puro_fp8_quant_act_128x1(_ptr(x), T, C, _ld(x), _ptr(qT), _ld(qT), _ptr(sT), _stream(stream)),
            "puro_fp8_quant_act_128x1")
     return qT, sT
+
+
+def puro_fp8_quant_act_dual(x, q=None, s=None, qT=None, sT=None, stream=None):
+    """x bf16 [T, C] -> (q [T, C], s [C/128, T], qT [C, T], sT [T/128, C]): the outputs of
+    puro_fp8_quant_act_1x128 and puro_fp8_quant_act_128x1 from one read of x."""
+    torch = _torch()
+    T, C = x.shape
+    if q is None:
+        q = torch.empty((T, C), dtype=torch.uint8, device=x.device)
+    if s is None:
+        s = torch.empty((C // 128, T), dtype=torch.float32, device=x.device)
+    if qT is None:
+        qT = torch.empty((C, T), dtype=torch.uint8, device=x.device)
+    if sT is None:
+        sT = torch.empty((T // 128, C), dtype=torch.float32, device=x.device)
+    _check(lib.puro_fp8_quant_act_dual(_ptr(x), T, C, _ld(x), _ptr(q), _ld(q), _ptr(s), _ptr(qT), _ld(qT),
+                                       _ptr(sT), _stream(stream)), "puro_fp8_quant_act_dual")
+    return q, s, qT, sT
 
 
 def puro_fp8_quant_w_128x128(w, q=None, s=None, qT=None, sT=None, transposed: bool = True, stream=None):

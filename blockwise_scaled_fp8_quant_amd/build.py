@@ -1,6 +1,8 @@
 """Build libpuro_fp8.so (gfx950) in-tree with hipcc.
 
-    python -m blockwise_scaled_fp8_quant_amd.build        # or build() from Python
+    python blockwise_scaled_fp8_quant_amd/build.py        # or __graft_entry__.build()
+
+(run as a file: importing it through the package would first load the library it builds)
 
 Objects go to <repo>/_build/, the shared library next to this file.  Every HIP source
 is compiled with packed-fp32 instruction generation disabled.

@@ -46,6 +46,18 @@ int puro_fp8_quant_act_128x1(const void* x, int64_t T, int64_t C, int64_t ldx, u
   return from_hip(puro::launch_quant_128x1(x, T, C, ldx, qT, ldqT, sT, st));
 }
 
+int puro_fp8_quant_act_dual(const void* x, int64_t T, int64_t C, int64_t ldx, uint8_t* q, int64_t ldq,
+                            float* s, uint8_t* qT, int64_t ldqT, float* sT, hipStream_t st) {
+  if (T < 0 || C < 0) return PURO_ERR_SHAPE;
+  if (T % kGroup || C % kGroup) return PURO_ERR_SHAPE;
+  if (T == 0 || C == 0) return PURO_OK;
+  if (!x || !q || !s || !qT || !sT) return PURO_ERR_NULLPTR;
+  if (!aligned16(x) || !aligned16(q) || !aligned16(s) || !aligned16(qT) || !aligned16(sT)) return PURO_ERR_ALIGN;
+  if (ldx < C || ldq < C || ldqT < T || (ldx * 2) % 16 || ldq % 16 || ldqT % 16) return PURO_ERR_LD;
+  if (T / kGroup > 65535) return PURO_ERR_UNSUPPORTED;
+  return from_hip(puro::launch_quant_dual(x, T, C, ldx, q, ldq, s, qT, ldqT, sT, st));
+}
+
 int puro_fp8_quant_w_128x128(const void* w, int64_t N, int64_t K, int64_t ldw, uint8_t* q, int64_t ldq,
                              float* s, uint8_t* qT, int64_t ldqT, float* sT, hipStream_t st) {
   if (N < 0 || K < 0) return PURO_ERR_SHAPE;

@@ -99,6 +99,15 @@ __device__ __forceinline__ uint32_t row16_max(uint32_t v) {
   return v;
 }
 
+// Packed 16-bit max over the 16 lanes of a DPP row (every lane receives the result).
+__device__ __forceinline__ uint32_t row16_pkmax(uint32_t v) {
+  v = pk_max_u16(v, dpp<kDppQuadXor1>(v));
+  v = pk_max_u16(v, dpp<kDppQuadXor2>(v));
+  v = pk_max_u16(v, dpp<kDppRowHalfMirror>(v));
+  v = pk_max_u16(v, dpp<kDppRowMirror>(v));
+  return v;
+}
+
 // Max over all 64 lanes of the wave.
 __device__ __forceinline__ uint32_t wave_max(uint32_t v) {
   v = row16_max(v);

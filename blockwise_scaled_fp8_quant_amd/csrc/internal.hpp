@@ -12,6 +12,8 @@ hipError_t launch_quant_1x128(const void* x, int64_t M, int64_t K, int64_t ldx, 
                               int64_t ldq, float* s, hipStream_t st);
 hipError_t launch_quant_128x1(const void* x, int64_t T, int64_t C, int64_t ldx, uint8_t* qT,
                               int64_t ldqT, float* sT, hipStream_t st);
+hipError_t launch_quant_dual(const void* x, int64_t T, int64_t C, int64_t ldx, uint8_t* q, int64_t ldq,
+                             float* s, uint8_t* qT, int64_t ldqT, float* sT, hipStream_t st);
 hipError_t launch_quant_128x128(const void* w, int64_t N, int64_t K, int64_t ldw, uint8_t* q,
                                 int64_t ldq, float* s, uint8_t* qT, int64_t ldqT, float* sT,
                                 hipStream_t st);

@@ -148,6 +148,126 @@ __global__ __launch_bounds__(256) void quant_128x1_kernel(const uint16_t* __rest
 }
 
 // ---------------------------------------------------------------------------------------
+// Dual 1x128 + 128x1 quantizer: one read of a bf16 [T, C] tensor yields both the row-wise
+// codes (1x128 groups along C; what quant_1x128_kernel writes) and the transposed
+// column-wise codes (128x1 groups along T; what quant_128x1_kernel writes), with their
+// scales.  A workgroup owns a 128-token x 128-column tile: one 1x128 group per token and
+// one 128x1 group per column.  Thread t holds tokens 8*(t>>4) .. +7 x columns 8*(t&15) .. +7
+// (eight 16-byte loads; the 16 lanes of a DPP row read one token's 256-byte segment).
+//   token amax:  packed max over the thread's 8 columns, then across the 16 lanes of the row;
+//   column amax: packed max over the thread's 8 tokens, then across the 4 thread rows of the
+//                wave, then across the 4 waves in LDS.
+// One thread per token and one per column turn the amaxes into scales (stored) and
+// reciprocals (shared through LDS).  Row codes leave directly (16 lanes write a token's
+// 128 bytes); transposed codes are staged through LDS ([column][token quad], odd row
+// stride) and leave as 128-byte rows written by 8 lanes with 16-byte stores.
+// ---------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void quant_dual_kernel(const uint16_t* __restrict__ x, int64_t T, int64_t C,
+                                                         int64_t ldx, uint8_t* __restrict__ q, int64_t ldq,
+                                                         float* __restrict__ s, uint8_t* __restrict__ qT,
+                                                         int64_t ldqT, float* __restrict__ sT) {
+  __shared__ uint32_t rowmax[64];          // token pairs, packed
+  __shared__ uint32_t colred[4][64];       // per wave, column pairs, packed
+  __shared__ float rrow[128], rcol[128];
+  __shared__ uint32_t stage[128 * 33];
+
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  const int tc = t & 15, tr = t >> 4;
+  const int64_t tb = blockIdx.y, g = blockIdx.x;
+  const int64_t tok0 = tb * 128 + tr * 8;
+  const int64_t col0 = g * 128 + tc * 8;
+
+  u32x4 v[8];
+  const uint16_t* xp = x + tok0 * ldx + col0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xp + i * ldx));
+
+  // token amax: rp[k] holds tokens 2k (low half) and 2k+1 (high half)
+  uint32_t rp[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    uint32_t m2[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const u32x4 w = v[2 * k + e];
+      const uint32_t m = pk_max_u16(pk_max_u16(abs2(w.x), abs2(w.y)), pk_max_u16(abs2(w.z), abs2(w.w)));
+      m2[e] = hmax16(m);
+    }
+    rp[k] = row16_pkmax(m2[0] | (m2[1] << 16));
+  }
+  if (tc < 4) rowmax[tr * 4 + tc] = tc == 0 ? rp[0] : tc == 1 ? rp[1] : tc == 2 ? rp[2] : rp[3];
+
+  // column amax: cm[d] holds columns 8 tc + 2d (low) and 8 tc + 2d + 1 (high)
+  uint32_t cm[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    uint32_t m = abs2(v[0][d]);
+#pragma unroll
+    for (int i = 1; i < 8; ++i) m = pk_max_u16(m, abs2(v[i][d]));
+    m = pk_max_u16(m, (uint32_t)__shfl_xor((int)m, 16));
+    m = pk_max_u16(m, (uint32_t)__shfl_xor((int)m, 32));
+    cm[d] = m;
+  }
+  if (lane < 16) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) colred[wave][tc * 4 + d] = cm[d];
+  }
+  __syncthreads();
+
+  if (t < 128) {                                   // token t of the tile
+    const uint32_t w = rowmax[t >> 1];
+    float sc, r;
+    tile_scale((t & 1) ? (w >> 16) : (w & 0xFFFFu), sc, r);
+    rrow[t] = r;
+    s[g * T + tb * 128 + t] = sc;
+  } else {                                         // column t - 128 of the tile
+    const int c = t - 128, idx = c >> 1;
+    const uint32_t w = pk_max_u16(pk_max_u16(colred[0][idx], colred[1][idx]),
+                                  pk_max_u16(colred[2][idx], colred[3][idx]));
+    float sc, r;
+    tile_scale((c & 1) ? (w >> 16) : (w & 0xFFFFu), sc, r);
+    rcol[c] = r;
+    sT[tb * C + g * 128 + c] = sc;
+  }
+  __syncthreads();
+
+  // row-wise codes: token i's 8 columns -> 8 bytes
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float r = rrow[tr * 8 + i];
+    const u32x4 w = v[i];
+    u32x2 o;
+    o.x = cvt4(bf16_lo(w.x) * r, bf16_hi(w.x) * r, bf16_lo(w.y) * r, bf16_hi(w.y) * r);
+    o.y = cvt4(bf16_lo(w.z) * r, bf16_hi(w.z) * r, bf16_lo(w.w) * r, bf16_hi(w.w) * r);
+    __builtin_nontemporal_store(o, reinterpret_cast<u32x2*>(q + (tok0 + i) * ldq + col0));
+  }
+  // column-wise codes: column j's 8 tokens -> two dwords of the staged transposed tile
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float r = rcol[tc * 8 + j];
+    float e[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t w = v[i][j >> 1];
+      e[i] = ((j & 1) ? bf16_hi(w) : bf16_lo(w)) * r;
+    }
+    stage[(tc * 8 + j) * 33 + 2 * tr] = cvt4(e[0], e[1], e[2], e[3]);
+    stage[(tc * 8 + j) * 33 + 2 * tr + 1] = cvt4(e[4], e[5], e[6], e[7]);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int cl = (t >> 3) + 32 * it;
+    const int part = t & 7;
+    const uint32_t* sp = stage + cl * 33 + part * 4;
+    const u32x4 o = {sp[0], sp[1], sp[2], sp[3]};
+    __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(qT + (g * 128 + cl) * ldqT + tb * 128 + part * 16));
+  }
+}
+
+// ---------------------------------------------------------------------------------------
 // 128x128 weight blocks.  One workgroup per block; thread t holds rows 8*(t>>4) .. +7 of
 // the block at columns 8*(t&15) .. +7 (8 coalesced 16-byte loads).  Block amax: packed
 // max in registers, DPP/cross-lane max in the wave, LDS across the 4 waves.  The thread's
@@ -260,6 +380,15 @@ hipError_t launch_quant_128x1(const void* x, int64_t T, int64_t C, int64_t ldx, 
   if (gx > 0x7FFFFFFF || gy > 65535) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(quant_128x1_kernel, dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, st,
                      static_cast<const uint16_t*>(x), T, C, ldx, qT, ldqT, sT);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_dual(const void* x, int64_t T, int64_t C, int64_t ldx, uint8_t* q, int64_t ldq,
+                             float* s, uint8_t* qT, int64_t ldqT, float* sT, hipStream_t st) {
+  const int64_t gx = C / 128, gy = T / 128;
+  if (gx > 0x7FFFFFFF || gy > 65535) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(quant_dual_kernel, dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, st,
+                     static_cast<const uint16_t*>(x), T, C, ldx, q, ldq, s, qT, ldqT, sT);
   return hipGetLastError();
 }
 

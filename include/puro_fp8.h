@@ -90,6 +90,20 @@ int puro_fp8_quant_act_128x1(const void* x, int64_t T, int64_t C, int64_t ldx,
                              uint8_t* qT, int64_t ldqT, float* sT, hipStream_t st);
 
 /*
+ * Dual quantizer: one read of x yields exactly what puro_fp8_quant_act_1x128(x) and
+ * puro_fp8_quant_act_128x1(x) write (same bytes, same scales).  In training, X and dY each
+ * feed one GEMM with 1x128 groups (FWD / DGRAD) and one with 128x1 groups (WGRAD), so both
+ * quantizations of the same tensor are needed (same passages as above).
+ *   x   : bf16 [T, C], row stride ldx (elements); T % 128 == 0; C % 128 == 0.
+ *   q   : uint8 codes [T, C], row stride ldq (bytes); s: fp32 [C/128][T] (1x128 layout).
+ *   qT  : uint8 codes [C, T], row stride ldqT (bytes); sT: fp32 [T/128][C] (128x1 layout).
+ * All four outputs are required.
+ */
+int puro_fp8_quant_act_dual(const void* x, int64_t T, int64_t C, int64_t ldx,
+                            uint8_t* q, int64_t ldq, float* s,
+                            uint8_t* qT, int64_t ldqT, float* sT, hipStream_t st);
+
+/*
  * 128x128 weight-block quantizer (agihunt digest, section 方法, FP8 bullet: weights in
  * 128x128 blocks), with an optional transposed copy for dgrad.
  *   w   : bf16 [N, K], row stride ldw (elements); N % 128 == 0, K % 128 == 0.

@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_header_and_binding_agree():
     decl = declared_functions()
-    assert len(decl) == 8
+    assert len(decl) == 9
     assert sorted(P.EXPORTED_SYMBOLS) == decl
 
 
@@ -71,6 +71,20 @@ def test_quant_128x1_validation():
     assert q128x1(x=None) == NULLPTR and q128x1(sT=None) == NULLPTR
     assert q128x1(qT=MIS) == ALIGN
     assert q128x1(ldx=32) == LD and q128x1(ldqT=128) == LD and q128x1(ldqT=264) == LD
+
+
+def qd(x=A16, T=256, C=256, ldx=256, q=A16, ldq=256, s=A16, qT=A16, ldqT=256, sT=A16):
+    return P.lib.puro_fp8_quant_act_dual(x, T, C, ldx, q, ldq, s, qT, ldqT, sT, None)
+
+
+def test_quant_dual_validation():
+    assert qd(T=0) == OK and qd(C=0) == OK
+    assert qd(T=100) == SHAPE and qd(C=64) == SHAPE and qd(T=-128) == SHAPE
+    for arg in ("x", "q", "s", "qT", "sT"):
+        assert qd(**{arg: None}) == NULLPTR, arg
+        assert qd(**{arg: MIS}) == ALIGN, arg
+    assert qd(ldx=128) == LD and qd(ldq=128) == LD and qd(ldqT=128) == LD
+    assert qd(ldx=260) == LD and qd(ldq=264) == LD and qd(ldqT=264) == LD
 
 
 def qw(w=A16, N=256, K=256, ldw=256, q=A16, ldq=256, s=A16, qT=A16, ldqT=256, sT=A16):

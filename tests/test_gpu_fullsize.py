@@ -1,0 +1,179 @@
+"""Full-size GPU parity at the layer-sweep shapes (16384 tokens; weights qkv 4096x2048,
+o 2048x2048, gate_up 12288x2048, down 2048x6144): every kernel the benchmark step launches,
+at the shapes and in the launch configuration it times, checked on sampled outputs that
+the oracle computes one by one.
+
+Inputs are generated on the GPU by torch's seeded generator with the workload's
+distributions: activations and gradients Student-t (nu = 3) in bf16, weights N(0, 0.02).
+GEMM operands are E4M3 codes from torch's own float8_e4m3fn cast of Student-t data
+scaled towards the E4M3 range, with log-uniform fp32 scales.  Only the sampled rows / token
+blocks travel to the host, where the oracle computes them.
+
+Bars: quantizers byte-identical on every sampled 128-token block (all 1x128 groups of its
+rows, all 128x1 groups of its columns) and 128-row weight block; GEMMs within 1e-3
+normalized error (plus the tighter 1e-4 + bf16 rounding bound) on sampled rows x columns.
+"""
+import numpy as np
+import pytest
+
+from gpu_util import assert_bytes_equal, host, normalized_error, say, torch
+from oracle import e4m3, gemm, quant
+
+pytestmark = pytest.mark.gpu
+
+TOKENS = 16384
+WEIGHTS = [("qkv", 4096, 2048), ("o", 2048, 2048), ("gate_up", 12288, 2048), ("down", 2048, 6144)]
+TOL, TIGHT = 1e-3, 1e-4
+
+
+@pytest.fixture(scope="module")
+def P():
+    import blockwise_scaled_fp8_quant_amd as P
+    assert torch().cuda.is_available(), "GPU test run without a GPU"
+    return P
+
+
+def gen(seed):
+    t = torch()
+    g = t.Generator(device="cuda")
+    g.manual_seed(seed)
+    return g
+
+
+def student_t_bf16(shape, seed, scale=1.0):
+    """Student-t (nu = 3) as normal / sqrt(chi2_3 / 3), chi2_3 = sum of 3 squared normals."""
+    t = torch()
+    g = gen(seed)
+    z = t.randn(shape, generator=g, device="cuda")
+    c = t.zeros(shape, device="cuda")
+    for _ in range(3):
+        c += t.randn(shape, generator=g, device="cuda") ** 2
+    x = z / t.sqrt(c / 3.0) * scale
+    return x.to(t.bfloat16)
+
+
+def bits_of(x_rows):
+    """bf16 device tensor -> uint16 host bits."""
+    t = torch()
+    return x_rows.contiguous().view(t.int16).cpu().numpy().view(np.uint16)
+
+
+def token_blocks(T, seed, n=3):
+    rng = np.random.default_rng(seed)
+    return sorted(rng.choice(T // 128, size=n, replace=False).tolist())
+
+
+# --------------------------------------------------------------------------- quantizers
+
+@pytest.mark.parametrize("wname,dout,din", WEIGHTS)
+def test_dual_quantizer_full_size_sampled(P, wname, dout, din):
+    t = torch()
+    for what, C, scale, seed in (("X", din, 1.0, 1), ("dY", dout, 1e-3, 2)):
+        say(f"[fullsize dual] {wname} {what} {TOKENS}x{C}")
+        x = student_t_bf16((TOKENS, C), seed * 100 + dout, scale)
+        q, s, qT, sT = P.puro_fp8_quant_act_dual(x)
+        t.cuda.synchronize()
+        for tb in token_blocks(TOKENS, C + seed):
+            rows = slice(128 * tb, 128 * tb + 128)
+            xb = bits_of(x[rows])
+            rq, rs = quant.quant_act_1x128(xb)
+            rqT, rsT = quant.quant_act_128x1(xb)
+            assert_bytes_equal(host(q[rows]), rq, f"{what} rows of block {tb}")
+            assert_bytes_equal(host(s[:, rows]), rs, f"{what} row scales of block {tb}")
+            assert_bytes_equal(host(qT[:, rows]), rqT, f"{what} transposed codes of block {tb}")
+            assert_bytes_equal(host(sT[tb:tb + 1]), rsT, f"{what} column scales of block {tb}")
+
+
+@pytest.mark.parametrize("wname,dout,din", WEIGHTS)
+def test_single_quantizers_full_size_sampled(P, wname, dout, din):
+    t = torch()
+    say(f"[fullsize 1x128 / 128x1] {wname} X {TOKENS}x{din}")
+    x = student_t_bf16((TOKENS, din), 7 + din)
+    q, s = P.puro_fp8_quant_act_1x128(x)
+    qT, sT = P.puro_fp8_quant_act_128x1(x)
+    t.cuda.synchronize()
+    for tb in token_blocks(TOKENS, din + 11):
+        rows = slice(128 * tb, 128 * tb + 128)
+        xb = bits_of(x[rows])
+        rq, rs = quant.quant_act_1x128(xb)
+        rqT, rsT = quant.quant_act_128x1(xb)
+        assert_bytes_equal(host(q[rows]), rq, f"1x128 rows of block {tb}")
+        assert_bytes_equal(host(s[:, rows]), rs, f"1x128 scales of block {tb}")
+        assert_bytes_equal(host(qT[:, rows]), rqT, f"128x1 codes of block {tb}")
+        assert_bytes_equal(host(sT[tb:tb + 1]), rsT, f"128x1 scales of block {tb}")
+
+
+@pytest.mark.parametrize("wname,dout,din", WEIGHTS)
+def test_weight_quantizer_full_size_sampled(P, wname, dout, din):
+    t = torch()
+    say(f"[fullsize 128x128] {wname} W {dout}x{din}")
+    g = gen(31 + dout)
+    w = (t.randn((dout, din), generator=g, device="cuda") * 0.02).to(t.bfloat16)
+    q, s, qT, sT = P.puro_fp8_quant_w_128x128(w)
+    t.cuda.synchronize()
+    for rb in token_blocks(dout, din, n=2):
+        rows = slice(128 * rb, 128 * rb + 128)
+        wb = bits_of(w[rows])
+        rq, rs, rqT, rsT = quant.quant_w_128x128(wb)
+        assert_bytes_equal(host(q[rows]), rq, f"codes of block row {rb}")
+        assert_bytes_equal(host(s[rb:rb + 1]), rs, f"scales of block row {rb}")
+        assert_bytes_equal(host(qT[:, rows]), rqT, f"transposed codes of block row {rb}")
+        assert_bytes_equal(host(sT[:, rb:rb + 1]), rsT, f"transposed scales of block row {rb}")
+
+
+# --------------------------------------------------------------------------- GEMMs
+
+def e4m3_codes(shape, seed):
+    """Codes of Student-t data scaled so that typical tiles use the upper E4M3 range."""
+    t = torch()
+    x = student_t_bf16(shape, seed, scale=64.0).float().clamp(-448.0, 448.0)
+    return x.to(t.float8_e4m3fn).view(t.uint8)
+
+
+def log_uniform_scales(shape, seed, lo=-14, hi=-2):
+    t = torch()
+    g = gen(seed)
+    return t.exp2(t.rand(shape, generator=g, device="cuda") * (hi - lo) + lo)
+
+
+def gemm_case(mode, M, N, K, seed):
+    A = e4m3_codes((M, K), seed)
+    B = e4m3_codes((N, K), seed + 1)
+    sA = log_uniform_scales((K // 128, M), seed + 2)
+    sB = log_uniform_scales((K // 128, N) if mode == "WGRAD" else (N // 128, K // 128), seed + 3)
+    return A, sA, B, sB
+
+
+@pytest.mark.parametrize("mode", ["FWD", "DGRAD", "WGRAD"])
+@pytest.mark.parametrize("wname,dout,din", WEIGHTS)
+def test_gemm_full_size_sampled(P, wname, dout, din, mode):
+    t = torch()
+    M, N, K = {"FWD": (TOKENS, dout, din), "DGRAD": (TOKENS, din, dout), "WGRAD": (dout, din, TOKENS)}[mode]
+    out_dtype = P.OUT_FP32 if mode == "WGRAD" else P.OUT_BF16
+    say(f"[fullsize gemm] {wname} {mode} M,N,K={M},{N},{K} out={'fp32' if out_dtype else 'bf16'}")
+    seed = 1000 * [w[0] for w in WEIGHTS].index(wname) + 10 * ["FWD", "DGRAD", "WGRAD"].index(mode)
+    A, sA, B, sB = gemm_case(mode, M, N, K, seed)
+    C = torch().empty((M, N), dtype=t.float32 if out_dtype else t.bfloat16, device="cuda")
+    P.puro_fp8_gemm(getattr(P, mode), A, sA, B, sB, C=C, out_dtype=out_dtype)
+    t.cuda.synchronize()
+    rng = np.random.default_rng(M + N + K)
+    rows = np.sort(rng.choice(M, size=96, replace=False))
+    cols = np.sort(rng.choice(N, size=96, replace=False))
+    rt, ct = t.from_numpy(rows).cuda(), t.from_numpy(cols).cuda()
+    Ah, sAh = host(A[rt]), host(sA[:, rt])
+    Bh = host(B[ct])
+    sBh = host(sB[:, ct]) if mode == "WGRAD" else host(sB)
+    Ad = gemm.dequant_a(Ah, sAh)
+    if mode == "WGRAD":
+        Bd = gemm.dequant_b(mode, Bh, sBh)
+    else:
+        Bd = e4m3.decode(Bh) * np.repeat(sBh[cols // 128].astype(np.float64), 128, axis=1)
+    ref = Ad @ Bd.T
+    sub = host(C[rt][:, ct])
+    na, nb = np.sqrt((Ad * Ad).sum(1)), np.sqrt((Bd * Bd).sum(1))
+    err, diff, den = normalized_error(sub, ref, na, nb)
+    say(f"    max normalized error {err:.3e}")
+    assert err <= TOL
+    bound = TIGHT * den + (2.0 ** -8 * np.abs(ref) * (1 + 2.0 ** -7) if out_dtype == P.OUT_BF16 else 0.0)
+    assert (diff <= bound).all()
+    assert bool(t.isfinite(C).all())
