@@ -61,6 +61,25 @@ __global__ __launch_bounds__(256) void quant_1x128_kernel(const uint16_t* __rest
   }
 }
 
+// Tile order of the transposing quantizers: workgroup b takes token block tb and column
+// block g such that runs of `bt` consecutive workgroups cover bt consecutive token blocks of
+// one column block.  Each transposed output row then receives bt x 128 contiguous bytes
+// from neighbouring workgroups (4 KB with bt = 32) instead of scattered 128-byte pieces,
+// which keeps HBM writes within open DRAM pages.  (Measured on MI355X, dual quantizer,
+// 16384 x 12288 bf16: 4.6 -> 5.3 TB/s.)
+__device__ __forceinline__ void tile_order(int64_t b, int64_t n_col_blocks, int bt, int64_t& tb, int64_t& g) {
+  const int64_t run = b / bt, r = b - run * bt;
+  tb = (run / n_col_blocks) * bt + r;
+  g = run % n_col_blocks;
+}
+
+// Token blocks per run: the largest power of two <= 32 dividing the number of token blocks.
+static inline int token_run(int64_t nb) {
+  int bt = 32;
+  while (nb % bt) bt >>= 1;
+  return bt;
+}
+
 // ---------------------------------------------------------------------------------------
 // 128x1, transposed output.  A workgroup owns 128 tokens x 64 columns.  Thread t holds
 // 4 consecutive tokens (4*(t>>3) .. +3) x 8 consecutive columns (8*(t&7) .. +7), loaded
@@ -75,7 +94,7 @@ __global__ __launch_bounds__(256) void quant_1x128_kernel(const uint16_t* __rest
 __global__ __launch_bounds__(256) void quant_128x1_kernel(const uint16_t* __restrict__ x, int64_t T,
                                                           int64_t C, int64_t ldx,
                                                           uint8_t* __restrict__ qT, int64_t ldqT,
-                                                          float* __restrict__ sT) {
+                                                          float* __restrict__ sT, int bt) {
   __shared__ uint32_t red[4][32];
   __shared__ float rsh[64];
   __shared__ uint32_t stage[64 * 33];
@@ -85,8 +104,9 @@ __global__ __launch_bounds__(256) void quant_128x1_kernel(const uint16_t* __rest
   const int wave = t >> 6;
   const int cc = t & 7;
   const int rq = t >> 3;
-  const int64_t tb = blockIdx.y;
-  const int64_t c0 = (int64_t)blockIdx.x * 64;
+  int64_t tb, cb;
+  tile_order(blockIdx.x, (C + 63) / 64, bt, tb, cb);
+  const int64_t c0 = cb * 64;
   const int64_t col = c0 + cc * 8;
   const bool ok = col < C;
 
@@ -165,7 +185,7 @@ __global__ __launch_bounds__(256) void quant_128x1_kernel(const uint16_t* __rest
 __global__ __launch_bounds__(256) void quant_dual_kernel(const uint16_t* __restrict__ x, int64_t T, int64_t C,
                                                          int64_t ldx, uint8_t* __restrict__ q, int64_t ldq,
                                                          float* __restrict__ s, uint8_t* __restrict__ qT,
-                                                         int64_t ldqT, float* __restrict__ sT) {
+                                                         int64_t ldqT, float* __restrict__ sT, int bt) {
   __shared__ uint32_t rowmax[64];          // token pairs, packed
   __shared__ uint32_t colred[4][64];       // per wave, column pairs, packed
   __shared__ float rrow[128], rcol[128];
@@ -175,7 +195,8 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(const uint16_t* __restr
   const int lane = t & 63;
   const int wave = t >> 6;
   const int tc = t & 15, tr = t >> 4;
-  const int64_t tb = blockIdx.y, g = blockIdx.x;
+  int64_t tb, g;
+  tile_order(blockIdx.x, C / 128, bt, tb, g);
   const int64_t tok0 = tb * 128 + tr * 8;
   const int64_t col0 = g * 128 + tc * 8;
 
@@ -376,19 +397,19 @@ hipError_t launch_quant_1x128(const void* x, int64_t M, int64_t K, int64_t ldx, 
 
 hipError_t launch_quant_128x1(const void* x, int64_t T, int64_t C, int64_t ldx, uint8_t* qT,
                               int64_t ldqT, float* sT, hipStream_t st) {
-  const int64_t gx = (C + 63) / 64, gy = T / 128;
-  if (gx > 0x7FFFFFFF || gy > 65535) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(quant_128x1_kernel, dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, st,
-                     static_cast<const uint16_t*>(x), T, C, ldx, qT, ldqT, sT);
+  const int64_t nc = (C + 63) / 64, nb = T / 128;
+  if (nc * nb > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(quant_128x1_kernel, dim3((unsigned)(nc * nb)), dim3(256), 0, st,
+                     static_cast<const uint16_t*>(x), T, C, ldx, qT, ldqT, sT, token_run(nb));
   return hipGetLastError();
 }
 
 hipError_t launch_quant_dual(const void* x, int64_t T, int64_t C, int64_t ldx, uint8_t* q, int64_t ldq,
                              float* s, uint8_t* qT, int64_t ldqT, float* sT, hipStream_t st) {
-  const int64_t gx = C / 128, gy = T / 128;
-  if (gx > 0x7FFFFFFF || gy > 65535) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(quant_dual_kernel, dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, st,
-                     static_cast<const uint16_t*>(x), T, C, ldx, q, ldq, s, qT, ldqT, sT);
+  const int64_t nb = T / 128, ng = C / 128;
+  if (nb * ng > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(quant_dual_kernel, dim3((unsigned)(nb * ng)), dim3(256), 0, st,
+                     static_cast<const uint16_t*>(x), T, C, ldx, q, ldq, s, qT, ldqT, sT, token_run(nb));
   return hipGetLastError();
 }
 
