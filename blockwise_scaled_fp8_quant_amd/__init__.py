@@ -16,8 +16,8 @@ from typing import Optional, Tuple
 __all__ = [
     "LIB_PATH", "lib", "PuroError", "FWD", "DGRAD", "WGRAD", "OUT_BF16", "OUT_FP32",
     "puro_fp8_quant_act_1x128", "puro_fp8_quant_act_128x1", "puro_fp8_quant_act_dual",
-    "puro_fp8_quant_w_128x128", "puro_fp8_gemm", "puro_fp8_gemm_workspace_size", "puro_fp8_cast_e4m3",
-    "puro_fp8_strerror", "puro_fp8_version", "EXPORTED_SYMBOLS",
+    "puro_fp8_quant_w_128x128", "puro_fp8_gemm", "puro_fp8_gemm_accumulate", "puro_fp8_gemm_workspace_size",
+    "puro_fp8_cast_e4m3", "puro_fp8_strerror", "puro_fp8_version", "EXPORTED_SYMBOLS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpuro_fp8.so")
@@ -28,7 +28,7 @@ MODE_NAMES = {"FWD": FWD, "DGRAD": DGRAD, "WGRAD": WGRAD}
 
 EXPORTED_SYMBOLS = (
     "puro_fp8_quant_act_1x128", "puro_fp8_quant_act_128x1", "puro_fp8_quant_act_dual", "puro_fp8_quant_w_128x128",
-    "puro_fp8_gemm", "puro_fp8_gemm_workspace_size", "puro_fp8_cast_e4m3",
+    "puro_fp8_gemm", "puro_fp8_gemm_accumulate", "puro_fp8_gemm_workspace_size", "puro_fp8_cast_e4m3",
     "puro_fp8_strerror", "puro_fp8_version",
 )
 
@@ -64,6 +64,7 @@ lib.puro_fp8_quant_act_128x1.argtypes = [_p, _i64, _i64, _i64, _p, _i64, _p, _p]
 lib.puro_fp8_quant_act_dual.argtypes = [_p, _i64, _i64, _i64, _p, _i64, _p, _p, _i64, _p, _p]
 lib.puro_fp8_quant_w_128x128.argtypes = [_p, _i64, _i64, _i64, _p, _i64, _p, _p, _i64, _p, _p]
 lib.puro_fp8_gemm.argtypes = [_int, _i64, _i64, _i64, _p, _i64, _p, _p, _i64, _p, _p, _i64, _int, _p, _sz, _p]
+lib.puro_fp8_gemm_accumulate.argtypes = [_int, _i64, _i64, _i64, _p, _i64, _p, _p, _i64, _p, _p, _i64, _p, _sz, _p]
 lib.puro_fp8_gemm_workspace_size.argtypes = [_int, _i64, _i64, _i64]
 lib.puro_fp8_gemm_workspace_size.restype = _sz
 lib.puro_fp8_cast_e4m3.argtypes = [_p, _i64, _p, _p]
@@ -195,6 +196,22 @@ def puro_fp8_gemm(mode, A, sA, B, sB, C=None, out_dtype: int = OUT_BF16, workspa
     wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib.puro_fp8_gemm(mode, M, N, K, _ptr(A), _ld(A), _ptr(sA), _ptr(B), _ld(B), _ptr(sB), _ptr(C), _ld(C),
                              out_dtype, _ptr(workspace), wbytes, _stream(stream)), "puro_fp8_gemm")
+    return C
+
+
+def puro_fp8_gemm_accumulate(mode, A, sA, B, sB, C, workspace=None, stream=None):
+    """C [M, N] fp32 += blockwise-scaled FP8 product of A [M, K] and B [N, K] (see puro_fp8.h)."""
+    torch = _torch()
+    if isinstance(mode, str):
+        mode = MODE_NAMES[mode]
+    M, K = A.shape
+    N = B.shape[0]
+    need = lib.puro_fp8_gemm_workspace_size(mode, M, N, K)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=A.device)
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.puro_fp8_gemm_accumulate(mode, M, N, K, _ptr(A), _ld(A), _ptr(sA), _ptr(B), _ld(B), _ptr(sB), _ptr(C),
+                                        _ld(C), _ptr(workspace), wbytes, _stream(stream)), "puro_fp8_gemm_accumulate")
     return C
 
 

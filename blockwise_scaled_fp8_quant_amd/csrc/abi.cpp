@@ -73,9 +73,9 @@ int puro_fp8_quant_w_128x128(const void* w, int64_t N, int64_t K, int64_t ldw, u
   return from_hip(puro::launch_quant_128x128(w, N, K, ldw, q, ldq, s, qT, ldqT, sT, st));
 }
 
-int puro_fp8_gemm(int mode, int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda, const float* sA,
-                  const uint8_t* B, int64_t ldb, const float* sB, void* C, int64_t ldc, int out_dtype,
-                  void* workspace, size_t workspace_bytes, hipStream_t st) {
+static int gemm_common(int mode, int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda, const float* sA,
+                       const uint8_t* B, int64_t ldb, const float* sB, void* C, int64_t ldc, int out_dtype,
+                       bool accumulate, void* workspace, size_t workspace_bytes, hipStream_t st) {
   if (mode != PURO_GEMM_FWD && mode != PURO_GEMM_DGRAD && mode != PURO_GEMM_WGRAD) return PURO_ERR_MODE;
   if (out_dtype != PURO_OUT_BF16 && out_dtype != PURO_OUT_FP32) return PURO_ERR_DTYPE;
   if (M < 0 || N < 0 || K < 0) return PURO_ERR_SHAPE;
@@ -94,7 +94,21 @@ int puro_fp8_gemm(int mode, int64_t M, int64_t N, int64_t K, const uint8_t* A, i
   const size_t need = puro::gemm_workspace_bytes(mode, M, N, K);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return PURO_ERR_WORKSPACE;
   return from_hip(puro::launch_gemm(mode, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, out_dtype == PURO_OUT_BF16,
-                                    workspace, workspace_bytes, st));
+                                    accumulate, workspace, workspace_bytes, st));
+}
+
+int puro_fp8_gemm(int mode, int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda, const float* sA,
+                  const uint8_t* B, int64_t ldb, const float* sB, void* C, int64_t ldc, int out_dtype,
+                  void* workspace, size_t workspace_bytes, hipStream_t st) {
+  return gemm_common(mode, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, out_dtype, false, workspace, workspace_bytes,
+                     st);
+}
+
+int puro_fp8_gemm_accumulate(int mode, int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
+                             const float* sA, const uint8_t* B, int64_t ldb, const float* sB, float* C, int64_t ldc,
+                             void* workspace, size_t workspace_bytes, hipStream_t st) {
+  return gemm_common(mode, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, PURO_OUT_FP32, true, workspace,
+                     workspace_bytes, st);
 }
 
 size_t puro_fp8_gemm_workspace_size(int mode, int64_t M, int64_t N, int64_t K) {

@@ -101,6 +101,7 @@ struct GemmArgs {
   const float* sB;
   void* C;
   int64_t ldc;
+  int accumulate;        // fp32 output only: C = C + result (one fp32 add per element)
 };
 
 // Map the linear workgroup id to a (tile_m, tile_n) pair: XCD-contiguous, grouped rows.  The
@@ -327,8 +328,13 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
 #pragma unroll
       for (int it = 0; it < 32 / kRowsPerIt; ++it) {
         const int r = it * kRowsPerIt + rr;
-        const g_u32x4 v = *reinterpret_cast<const g_u32x4*>(wbuf + r * kRow + rc * 16);
-        *reinterpret_cast<g_u32x4*>(cbase + (int64_t)r * p.ldc * kEs + rc * 16) = v;
+        g_u32x4 v = *reinterpret_cast<const g_u32x4*>(wbuf + r * kRow + rc * 16);
+        g_u32x4* cp = reinterpret_cast<g_u32x4*>(cbase + (int64_t)r * p.ldc * kEs + rc * 16);
+        if (!OUT_BF16 && p.accumulate) {
+          const g_f32x4 sum = __builtin_bit_cast(g_f32x4, v) + __builtin_bit_cast(g_f32x4, *cp);
+          v = __builtin_bit_cast(g_u32x4, sum);
+        }
+        *cp = v;
       }
     }
     __builtin_amdgcn_s_waitcnt(0);
@@ -346,11 +352,11 @@ __global__ __launch_bounds__(256) void zero_fill_kernel(void* __restrict__ C, in
 }
 
 // Sum of the fp32 partials of a split contraction, in split order (deterministic), written as
-// bf16 (round to nearest even) or fp32.  4 consecutive columns per thread.
+// bf16 (round to nearest even) or fp32 (optionally added to C).  4 consecutive columns per thread.
 template <bool OUT_BF16>
 __global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restrict__ part, int splits,
                                                            int64_t split_stride, int M, int N,
-                                                           void* __restrict__ C, int64_t ldc) {
+                                                           void* __restrict__ C, int64_t ldc, int accumulate) {
   const int64_t n4 = N >> 2;
   const int64_t total = (int64_t)M * n4;
   for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (int64_t)gridDim.x * blockDim.x) {
@@ -363,7 +369,9 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restri
       o[1] = bf16x2_rne(acc[2], acc[3]);
       *reinterpret_cast<g_u32x2*>(static_cast<uint16_t*>(C) + i * ldc + j) = o;
     } else {
-      *reinterpret_cast<g_f32x4*>(static_cast<float*>(C) + i * ldc + j) = acc;
+      g_f32x4* cp = reinterpret_cast<g_f32x4*>(static_cast<float*>(C) + i * ldc + j);
+      if (accumulate) acc = acc + *cp;   // after the in-order sum: the same single add as unsplit
+      *cp = acc;
     }
   }
 }
@@ -422,8 +430,12 @@ static int choose_group(int64_t M, int64_t N, int64_t K) {
 
 hipError_t launch_gemm(int mode, int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
                        const float* sA, const uint8_t* B, int64_t ldb, const float* sB, void* C,
-                       int64_t ldc, bool out_bf16, void* workspace, size_t workspace_bytes, hipStream_t st) {
+                       int64_t ldc, bool out_bf16, bool accumulate, void* workspace, size_t workspace_bytes,
+                       hipStream_t st) {
+  if (accumulate && out_bf16) return hipErrorInvalidValue;
   if (K == 0) {
+    if (accumulate) return hipSuccess;   // C + 0
+
     const int64_t es = out_bf16 ? 2 : 4;
     const int64_t gy = M < 65535 ? M : 65535;
     hipLaunchKernelGGL(zero_fill_kernel, dim3(8, (unsigned)gy), dim3(256), 0, st, C, M, N * es, ldc * es);
@@ -435,6 +447,7 @@ hipError_t launch_gemm(int mode, int64_t M, int64_t N, int64_t K, const uint8_t*
   a.tiles_n = (int)((N + kBN - 1) / kBN);
   if ((int64_t)a.tiles_m * a.tiles_n > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   a.A = A; a.lda = lda; a.sA = sA; a.B = B; a.ldb = ldb; a.sB = sB; a.C = C; a.ldc = ldc;
+  a.accumulate = 0;
   a.splits = choose_splits(M, N, K);
   a.group = choose_group(M, N, K);
   a.kb_per_split = (int)((K / kBK + a.splits - 1) / a.splits);
@@ -456,12 +469,14 @@ hipError_t launch_gemm(int mode, int64_t M, int64_t N, int64_t K, const uint8_t*
     const int64_t blocks = std::min<int64_t>((work + 255) / 256, 4096);
     if (out_bf16)
       hipLaunchKernelGGL(split_reduce_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, st,
-                         static_cast<const float*>(workspace), a.splits, a.split_stride, (int)M, (int)N, C, ldc);
+                         static_cast<const float*>(workspace), a.splits, a.split_stride, (int)M, (int)N, C, ldc, 0);
     else
       hipLaunchKernelGGL(split_reduce_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, st,
-                         static_cast<const float*>(workspace), a.splits, a.split_stride, (int)M, (int)N, C, ldc);
+                         static_cast<const float*>(workspace), a.splits, a.split_stride, (int)M, (int)N, C, ldc,
+                         accumulate ? 1 : 0);
     return hipGetLastError();
   }
+  a.accumulate = accumulate ? 1 : 0;
   switch (mode * 2 + (out_bf16 ? 1 : 0)) {
     case 0: return launch_one<0, false>(a, st);
     case 1: return launch_one<0, true>(a, st);

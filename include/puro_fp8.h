@@ -139,7 +139,22 @@ int puro_fp8_gemm(int mode, int64_t M, int64_t N, int64_t K,
                   void* C, int64_t ldc, int out_dtype,
                   void* workspace, size_t workspace_bytes, hipStream_t st);
 
-/* Bytes of workspace puro_fp8_gemm needs for this problem (0 = none). */
+/*
+ * Accumulating variant, fp32 output only: C[i,j] = fl32(C[i,j] + P[i,j]), where P is exactly the
+ * fp32 result puro_fp8_gemm writes for the same arguments (one fp32 addition per element).
+ * For accumulating the fp32 weight gradient over micro-batches: the pages keep master weights
+ * and optimizer state in BF16/FP32 (agihunt digest, section 方法, FP8 bullet) and train with a
+ * global batch of 1536 sequences of 4096 tokens (same section, training layout), far more
+ * tokens than one WGRAD call takes.  Arguments, layouts and errors as puro_fp8_gemm, with
+ * out_dtype fixed to PURO_OUT_FP32; C is read and written.  K == 0 leaves C unchanged.
+ */
+int puro_fp8_gemm_accumulate(int mode, int64_t M, int64_t N, int64_t K,
+                             const uint8_t* A, int64_t lda, const float* sA,
+                             const uint8_t* B, int64_t ldb, const float* sB,
+                             float* C, int64_t ldc,
+                             void* workspace, size_t workspace_bytes, hipStream_t st);
+
+/* Bytes of workspace puro_fp8_gemm and puro_fp8_gemm_accumulate need for this problem (0 = none). */
 size_t puro_fp8_gemm_workspace_size(int mode, int64_t M, int64_t N, int64_t K);
 
 /*

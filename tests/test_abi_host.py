@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_header_and_binding_agree():
     decl = declared_functions()
-    assert len(decl) == 9
+    assert len(decl) == 10
     assert sorted(P.EXPORTED_SYMBOLS) == decl
 
 
@@ -132,6 +132,24 @@ def test_workspace_query():
     for mode in (0, 1, 2):
         assert P.puro_fp8_gemm_workspace_size(mode, 0, 128, 128) == 0
         assert P.puro_fp8_gemm_workspace_size(mode, 4096, 4096, 2048) >= 0
+
+
+def ga(mode=2, M=256, N=256, K=256, A=A16, lda=256, sA=A16, B=A16, ldb=256, sB=A16, C=A16, ldc=256,
+       ws=None, wsb=0):
+    return P.lib.puro_fp8_gemm_accumulate(mode, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, ws, wsb, None)
+
+
+def test_gemm_accumulate_validation():
+    # same checks as puro_fp8_gemm with an fp32 C (ld rule in 4-byte elements)
+    assert ga(M=0) == OK and ga(N=0) == OK
+    assert ga(mode=5) == MODE
+    assert ga(M=200) == SHAPE and ga(K=-128) == SHAPE
+    assert ga(C=None) == NULLPTR and ga(B=None) == NULLPTR
+    assert ga(C=MIS) == ALIGN and ga(sB=A16 + 8) == ALIGN
+    assert ga(ldc=255) == LD and ga(ldc=258) == LD and ga(lda=100) == LD
+    need = P.puro_fp8_gemm_workspace_size(2, 2048, 2048, 16384)
+    assert ga(M=2048, N=2048, K=16384, lda=16384, ldb=16384, ldc=2048) == WORKSPACE
+    assert ga(M=2048, N=2048, K=16384, lda=16384, ldb=16384, ldc=2048, ws=A16, wsb=need - 1) == WORKSPACE
 
 
 def test_cast_validation():
