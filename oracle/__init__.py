@@ -25,7 +25,15 @@ Pins (checked by the ``-m "not gpu"`` tests, against things other than this code
                       cases (unit scales -> plain FP8 matmul; one nonzero code per
                       row -> one scaled product; scaled small integers -> exact
                       integer result).
+  mx.*                MXFP8 (OCP MX v1.0, E4M3 elements, blocks of 32): E8M0 decode
+                      against PyTorch's float8_e8m0fnu for all 256 codes; the shared
+                      exponent against a brute-force power-of-two search for every
+                      finite bf16 amax; block maxima land in [256, 512) and the
+                      reconstruction error stays within half an E4M3 ulp (or the
+                      saturation distance); scaled small integers are exact; the
+                      GEMM against pure-Python triple loops and, with unit scales,
+                      the plain FP8 matmul.
 Parity unpinned: agreement with Puro's own training numerics (their scale
 format, their MXFP8 path) -- the pages print no code, values or error figures.
 """
-from . import e4m3, gemm, quant  # noqa: F401
+from . import e4m3, gemm, mx, quant  # noqa: F401
