@@ -11,7 +11,9 @@ Inputs are seeded synthetic bf16 tensors already resident in HBM when timing sta
 Prints ONE JSON line.  `value` = GEMM TFLOP/s of the whole step (all 12 GEMMs' flops
 divided by the step time, quantizers included in the time).  After the timed steps the
 standalone 1x128 and 128x1 quantizers are timed on the same tensors (reported under
-`kernels` with "in_step": false; not part of `value`).
+`kernels` with "in_step": false; not part of `value`), and so is the MXFP8 variant of the
+whole step (`mx_variant`: blocks of 32 with E8M0 scales; W, X and dY through the MX dual
+quantizer, then the three GEMMs).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
 
@@ -62,6 +64,10 @@ def kernel_source_hash() -> str:
 
 def op_of_kernel(name: str, last_gemm):
     """Map a dispatched kernel's name to the bench op it belongs to (None: not a path kernel)."""
+    if "mx_quant_dual" in name:
+        return "mx_quant_dual"
+    if "gemm_kernel<3" in name:
+        return "mx_gemm"
     if "gemm_kernel<0" in name:
         return "gemm_fwd"
     if "gemm_kernel<1" in name:
@@ -168,7 +174,7 @@ def build_step(P, torch, d):
     weight) list, the standalone single-quantizer list timed after the step, and the buffers."""
     from workloads import SWEEP_WEIGHTS
     dev = "cuda:0"
-    ops, single = [], []
+    ops, single, mxops = [], [], []
 
     def bf16(b):
         import numpy as np
@@ -201,13 +207,28 @@ def build_step(P, torch, d):
             ("gemm_dgrad", lambda Gq=Gq, Gs=Gs, WqT=WqT, WsT=WsT, dX=dX: P.puro_fp8_gemm(P.DGRAD, Gq, Gs, WqT, WsT, C=dX, out_dtype=P.OUT_BF16), gf(T, din, dout, 2), wname),
             ("gemm_wgrad", lambda GqT=GqT, GsT=GsT, XqT=XqT, XsT=XsT, dW=dW: P.puro_fp8_gemm(P.WGRAD, GqT, GsT, XqT, XsT, C=dW, out_dtype=P.OUT_FP32), gf(dout, din, T, 4), wname),
         ]
+        # MXFP8 variant of the same step (blocks of 32, E8M0 scales): W, X, dY each through the
+        # MX dual quantizer (both orientations), then the three GEMMs on the MX operands
+        mWq, mWx, mWqT, mWxT = u8(dout, din), u8(din // 128, dout, 4), u8(din, dout), u8(dout // 128, din, 4)
+        mXq, mXx, mXqT, mXxT = u8(T, din), u8(din // 128, T, 4), u8(din, T), u8(T // 128, din, 4)
+        mGq, mGx, mGqT, mGxT = u8(T, dout), u8(dout // 128, T, 4), u8(dout, T), u8(T // 128, dout, 4)
+        keep += [mWq, mWx, mWqT, mWxT, mXq, mXx, mXqT, mXxT, mGq, mGx, mGqT, mGxT]
+        mqb = lambda n: {"kind": "quant", "bytes": 2 * n + 2 * n + 2 * (n // 32)}
+        mxops += [
+            ("mx_quant_dual", lambda W=W, a=mWq, b=mWx, c=mWqT, e=mWxT: P.puro_fp8_mx_quant_dual(W, a, b, c, e), mqb(dout * din), wname),
+            ("mx_quant_dual", lambda X=X, a=mXq, b=mXx, c=mXqT, e=mXxT: P.puro_fp8_mx_quant_dual(X, a, b, c, e), mqb(T * din), wname),
+            ("mx_gemm_fwd", lambda a=mXq, b=mXx, c=mWq, e=mWx, Y=Y: P.puro_fp8_mx_gemm(a, b, c, e, C=Y, out_dtype=P.OUT_BF16), gf(T, dout, din, 2), wname),
+            ("mx_quant_dual", lambda dY=dY, a=mGq, b=mGx, c=mGqT, e=mGxT: P.puro_fp8_mx_quant_dual(dY, a, b, c, e), mqb(T * dout), wname),
+            ("mx_gemm_dgrad", lambda a=mGq, b=mGx, c=mWqT, e=mWxT, dX=dX: P.puro_fp8_mx_gemm(a, b, c, e, C=dX, out_dtype=P.OUT_BF16), gf(T, din, dout, 2), wname),
+            ("mx_gemm_wgrad", lambda a=mGqT, b=mGxT, c=mXqT, e=mXxT, dW=dW: P.puro_fp8_mx_gemm(a, b, c, e, C=dW, out_dtype=P.OUT_FP32), gf(dout, din, T, 4), wname),
+        ]
         single += [
             ("quant_act_1x128", lambda X=X, Xq=Xq, Xs=Xs: P.puro_fp8_quant_act_1x128(X, Xq, Xs), qb(T * din), wname),
             ("quant_act_1x128", lambda dY=dY, Gq=Gq, Gs=Gs: P.puro_fp8_quant_act_1x128(dY, Gq, Gs), qb(T * dout), wname),
             ("quant_act_128x1", lambda dY=dY, GqT=GqT, GsT=GsT: P.puro_fp8_quant_act_128x1(dY, GqT, GsT), qb(T * dout), wname),
             ("quant_act_128x1", lambda X=X, XqT=XqT, XsT=XsT: P.puro_fp8_quant_act_128x1(X, XqT, XsT), qb(T * din), wname),
         ]
-    return ops, single, keep
+    return ops, single, mxops, keep
 
 
 def cpu_baseline(d, tokens: int):
@@ -269,7 +290,7 @@ def main():
     t0 = time.time()
     d = draw(WORKLOAD)
     log(f"  drawn in {time.time() - t0:.1f} s")
-    ops, single, keep = build_step(P, torch, d)
+    ops, single, mxops, keep = build_step(P, torch, d)
     stream = torch.cuda.current_stream()
 
     # calibration copy for the HBM-traffic counters (untimed; reads and writes COPY_BYTES)
@@ -342,6 +363,15 @@ def main():
     single_ms, single_per = timed(single, args.steps)
     kernels.update(rows(single_per, single_ms, args.steps, False))
 
+    # the MXFP8 variant of the step, timed the same way (not part of `value`)
+    for _ in range(args.warmup):
+        run(mxops)
+    mx_ms, mx_per = timed(mxops, args.steps)
+    mx_step_ms = mx_ms / args.steps
+    mx_variant = {"ms_per_step": round(mx_step_ms, 4),
+                  "gemm_TFLOP/s_per_step": round(sum(w.get("flops", 0) for _, _, w, _ in mxops) / (mx_step_ms / 1e3) / 1e12, 2),
+                  "kernels": rows(mx_per, mx_ms, args.steps, True)}
+
     gemm_flops = sum(w.get("flops", 0) for _, _, w, _ in ops)
     value = gemm_flops / (ms_per_step / 1e3) / 1e12
     dom = max(per, key=lambda n: sum(per[n]["ms"]))
@@ -376,7 +406,7 @@ def main():
                                "1x128+128x1 quantization, fwd+dgrad+wgrad",
                    "tokens": 16384, "gemm_gflop_per_step": round(gemm_flops / 1e9, 1),
                    "parallelism": "single GPU"},
-        "roofline": roof, "cpu_baseline": cpu, "kernels": kernels,
+        "roofline": roof, "cpu_baseline": cpu, "kernels": kernels, "mx_variant": mx_variant,
     }
     print(json.dumps(out), flush=True)
     del keep

@@ -18,6 +18,7 @@ __all__ = [
     "puro_fp8_quant_act_1x128", "puro_fp8_quant_act_128x1", "puro_fp8_quant_act_dual",
     "puro_fp8_quant_w_128x128", "puro_fp8_gemm", "puro_fp8_gemm_accumulate", "puro_fp8_gemm_workspace_size",
     "puro_fp8_cast_e4m3", "puro_fp8_strerror", "puro_fp8_version", "EXPORTED_SYMBOLS",
+    "puro_fp8_mx_quant_dual", "puro_fp8_mx_gemm", "puro_fp8_mx_gemm_workspace_size",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpuro_fp8.so")
@@ -30,6 +31,7 @@ EXPORTED_SYMBOLS = (
     "puro_fp8_quant_act_1x128", "puro_fp8_quant_act_128x1", "puro_fp8_quant_act_dual", "puro_fp8_quant_w_128x128",
     "puro_fp8_gemm", "puro_fp8_gemm_accumulate", "puro_fp8_gemm_workspace_size", "puro_fp8_cast_e4m3",
     "puro_fp8_strerror", "puro_fp8_version",
+    "puro_fp8_mx_quant_dual", "puro_fp8_mx_gemm", "puro_fp8_mx_gemm_workspace_size",
 )
 
 if not os.path.exists(LIB_PATH):
@@ -65,6 +67,10 @@ lib.puro_fp8_quant_act_dual.argtypes = [_p, _i64, _i64, _i64, _p, _i64, _p, _p, 
 lib.puro_fp8_quant_w_128x128.argtypes = [_p, _i64, _i64, _i64, _p, _i64, _p, _p, _i64, _p, _p]
 lib.puro_fp8_gemm.argtypes = [_int, _i64, _i64, _i64, _p, _i64, _p, _p, _i64, _p, _p, _i64, _int, _p, _sz, _p]
 lib.puro_fp8_gemm_accumulate.argtypes = [_int, _i64, _i64, _i64, _p, _i64, _p, _p, _i64, _p, _p, _i64, _p, _sz, _p]
+lib.puro_fp8_mx_quant_dual.argtypes = [_p, _i64, _i64, _i64, _p, _i64, _p, _p, _i64, _p, _p]
+lib.puro_fp8_mx_gemm.argtypes = [_i64, _i64, _i64, _p, _i64, _p, _p, _i64, _p, _p, _i64, _int, _p, _sz, _p]
+lib.puro_fp8_mx_gemm_workspace_size.argtypes = [_i64, _i64, _i64]
+lib.puro_fp8_mx_gemm_workspace_size.restype = _sz
 lib.puro_fp8_gemm_workspace_size.argtypes = [_int, _i64, _i64, _i64]
 lib.puro_fp8_gemm_workspace_size.restype = _sz
 lib.puro_fp8_cast_e4m3.argtypes = [_p, _i64, _p, _p]
@@ -213,6 +219,41 @@ def puro_fp8_gemm_accumulate(mode, A, sA, B, sB, C, workspace=None, stream=None)
     _check(lib.puro_fp8_gemm_accumulate(mode, M, N, K, _ptr(A), _ld(A), _ptr(sA), _ptr(B), _ld(B), _ptr(sB), _ptr(C),
                                         _ld(C), _ptr(workspace), wbytes, _stream(stream)), "puro_fp8_gemm_accumulate")
     return C
+
+
+def puro_fp8_mx_quant_dual(x, q=None, xs=None, qT=None, xsT=None, stream=None):
+    """x bf16 [T, C] -> (q [T, C], xs uint8 [C/128, T, 4], qT [C, T], xsT uint8 [T/128, C, 4]): MXFP8
+    codes and E8M0 block scales along C and, transposed, along T."""
+    torch = _torch()
+    T, C = x.shape
+    u8 = lambda *s: torch.empty(s, dtype=torch.uint8, device=x.device)
+    q = u8(T, C) if q is None else q
+    xs = u8(C // 128, T, 4) if xs is None else xs
+    qT = u8(C, T) if qT is None else qT
+    xsT = u8(T // 128, C, 4) if xsT is None else xsT
+    _check(lib.puro_fp8_mx_quant_dual(_ptr(x), T, C, _ld(x), _ptr(q), _ld(q), _ptr(xs), _ptr(qT), _ld(qT),
+                                      _ptr(xsT), _stream(stream)), "puro_fp8_mx_quant_dual")
+    return q, xs, qT, xsT
+
+
+def puro_fp8_mx_gemm(A, xa, B, xb, C=None, out_dtype: int = OUT_BF16, workspace=None, stream=None):
+    """C [M, N] = MXFP8 product of A [M, K] (scales xa [K/128, M, 4]) and B [N, K] (xb [K/128, N, 4])."""
+    torch = _torch()
+    M, K = A.shape
+    N = B.shape[0]
+    if C is None:
+        C = torch.empty((M, N), dtype=torch.bfloat16 if out_dtype == OUT_BF16 else torch.float32, device=A.device)
+    need = lib.puro_fp8_mx_gemm_workspace_size(M, N, K)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=A.device)
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.puro_fp8_mx_gemm(M, N, K, _ptr(A), _ld(A), _ptr(xa), _ptr(B), _ld(B), _ptr(xb), _ptr(C), _ld(C),
+                                out_dtype, _ptr(workspace), wbytes, _stream(stream)), "puro_fp8_mx_gemm")
+    return C
+
+
+def puro_fp8_mx_gemm_workspace_size(M: int, N: int, K: int) -> int:
+    return int(lib.puro_fp8_mx_gemm_workspace_size(M, N, K))
 
 
 def puro_fp8_cast_e4m3(v, q=None, stream=None):

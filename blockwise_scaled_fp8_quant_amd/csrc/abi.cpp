@@ -10,6 +10,7 @@ namespace {
 
 constexpr int64_t kGroup = 128;
 constexpr int64_t kIntMax = 0x7FFFFFFF;
+constexpr int kModeMx = 3;   // the MXFP8 GEMM's internal mode (not a public PURO_GEMM_* value)
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -76,7 +77,8 @@ int puro_fp8_quant_w_128x128(const void* w, int64_t N, int64_t K, int64_t ldw, u
 static int gemm_common(int mode, int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda, const float* sA,
                        const uint8_t* B, int64_t ldb, const float* sB, void* C, int64_t ldc, int out_dtype,
                        bool accumulate, void* workspace, size_t workspace_bytes, hipStream_t st) {
-  if (mode != PURO_GEMM_FWD && mode != PURO_GEMM_DGRAD && mode != PURO_GEMM_WGRAD) return PURO_ERR_MODE;
+  if (mode != PURO_GEMM_FWD && mode != PURO_GEMM_DGRAD && mode != PURO_GEMM_WGRAD && mode != kModeMx)
+    return PURO_ERR_MODE;
   if (out_dtype != PURO_OUT_BF16 && out_dtype != PURO_OUT_FP32) return PURO_ERR_DTYPE;
   if (M < 0 || N < 0 || K < 0) return PURO_ERR_SHAPE;
   if (M % kGroup || N % kGroup || K % kGroup) return PURO_ERR_SHAPE;
@@ -100,8 +102,31 @@ static int gemm_common(int mode, int64_t M, int64_t N, int64_t K, const uint8_t*
 int puro_fp8_gemm(int mode, int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda, const float* sA,
                   const uint8_t* B, int64_t ldb, const float* sB, void* C, int64_t ldc, int out_dtype,
                   void* workspace, size_t workspace_bytes, hipStream_t st) {
+  if (mode == kModeMx) return PURO_ERR_MODE;   // internal mode: puro_fp8_mx_gemm
   return gemm_common(mode, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, out_dtype, false, workspace, workspace_bytes,
                      st);
+}
+
+int puro_fp8_mx_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda, const uint8_t* xa,
+                     const uint8_t* B, int64_t ldb, const uint8_t* xb, void* C, int64_t ldc, int out_dtype,
+                     void* workspace, size_t workspace_bytes, hipStream_t st) {
+  return gemm_common(kModeMx, M, N, K, A, lda, reinterpret_cast<const float*>(xa), B, ldb,
+                     reinterpret_cast<const float*>(xb), C, ldc, out_dtype, false, workspace, workspace_bytes, st);
+}
+
+size_t puro_fp8_mx_gemm_workspace_size(int64_t M, int64_t N, int64_t K) {
+  return puro::gemm_workspace_bytes(kModeMx, M, N, K);
+}
+
+int puro_fp8_mx_quant_dual(const void* x, int64_t T, int64_t C, int64_t ldx, uint8_t* q, int64_t ldq, uint8_t* xs,
+                           uint8_t* qT, int64_t ldqT, uint8_t* xsT, hipStream_t st) {
+  if (T < 0 || C < 0) return PURO_ERR_SHAPE;
+  if (T % kGroup || C % kGroup) return PURO_ERR_SHAPE;
+  if (T == 0 || C == 0) return PURO_OK;
+  if (!x || !q || !xs || !qT || !xsT) return PURO_ERR_NULLPTR;
+  if (!aligned16(x) || !aligned16(q) || !aligned16(xs) || !aligned16(qT) || !aligned16(xsT)) return PURO_ERR_ALIGN;
+  if (ldx < C || ldq < C || ldqT < T || (ldx * 2) % 16 || ldq % 16 || ldqT % 16) return PURO_ERR_LD;
+  return from_hip(puro::launch_mx_quant_dual(x, T, C, ldx, q, ldq, xs, qT, ldqT, xsT, st));
 }
 
 int puro_fp8_gemm_accumulate(int mode, int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,

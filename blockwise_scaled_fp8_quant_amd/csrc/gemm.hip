@@ -48,6 +48,7 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) void glb_void;
 
 constexpr int kBM = 256, kBN = 256, kBK = 128;
+constexpr int kModeMx = 3;     // MXFP8: E8M0 scales per 32-element block, applied by the scaled MFMA
 constexpr int kThreads = 512;
 constexpr int kStageA = kBM * kBK;              // 32 KB
 constexpr int kStageB = kBN * kBK;              // 32 KB
@@ -181,6 +182,14 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
 
   auto issue_scales = [&](int kb, int stage) {
     uint8_t* st = smem + stage * kStageBytes;
+    if constexpr (MODE == kModeMx) {
+      // E8M0 tiles: [K/128][rows][4] bytes; 256 rows x 4 bytes = 1 KB per operand per slice
+      const uint8_t* xa = reinterpret_cast<const uint8_t*>(p.sA);
+      const uint8_t* xb = reinterpret_cast<const uint8_t*>(p.sB);
+      if (wave == 0) g2lds16(xa + ((int64_t)kb * p.M + s_m) * 4, st + kStageA + kStageB);
+      if (wave == 1) g2lds16(xb + ((int64_t)kb * p.N + s_n) * 4, st + kStageA + kStageB + 1024);
+      return;
+    }
     if (wave == 0) g2lds16(p.sA + (int64_t)kb * p.M + s_m, st + kStageA + kStageB);
     if (wave == 1) {
       if (MODE == 2)
@@ -213,8 +222,16 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
   // fragment reads: lane reads 64 bytes (chunks 4h .. 4h+3) of row r; the swizzle term of
   // every row this lane reads is (l32 >> 1) & 7 (tile row offsets are multiples of 32)
   const int fsw = (l32 >> 1) & 7;
-  const int fcol[4] = {((4 * h + 0) ^ fsw) << 4, ((4 * h + 1) ^ fsw) << 4, ((4 * h + 2) ^ fsw) << 4,
-                       ((4 * h + 3) ^ fsw) << 4};
+  // Which 16-byte chunks of the slice a lane feeds.  Blockwise modes: chunks 4h .. 4h+3 (any
+  // order that A and B share gives the same slice sum).  MX: within one scaled MFMA, the
+  // 16-byte groups g = 0, 1 of both lane halves form two 32-element scale blocks, block g taking
+  // its scale from lane half g (measured on gfx950).  Lane half h therefore feeds chunks h,
+  // h + 4 (first MFMA: MX blocks 0 and 2) and h + 2, h + 6 (second MFMA: MX blocks 1 and 3), so
+  // that each hardware block is one MX block and lane half h supplies the scales of MX blocks
+  // 2h and 2h + 1, one 16-bit read.
+  const int fch[4] = {MODE == kModeMx ? h : 4 * h, MODE == kModeMx ? h + 4 : 4 * h + 1,
+                      MODE == kModeMx ? h + 2 : 4 * h + 2, MODE == kModeMx ? h + 6 : 4 * h + 3};
+  const int fcol[4] = {(fch[0] ^ fsw) << 4, (fch[1] ^ fsw) << 4, (fch[2] ^ fsw) << 4, (fch[3] ^ fsw) << 4};
 
   // product of the last tile of a slice, promoted by the next slice's block (WGRAD: together
   // with the column scales of the last column tile)
@@ -233,8 +250,12 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
 
     // row scales of the lane's two rows; FWD/DGRAD fold in the 128x128 weight-block scale
     // (the wave's 128 columns lie in one block, index wn)
-    const float sbb = (MODE != 2) ? sBs[wn] : 1.0f;
-    const float sc0 = sAs[wm * 64 + l32] * sbb, sc1 = sAs[wm * 64 + 32 + l32] * sbb;
+    float sc0 = 0.0f, sc1 = 0.0f;
+    if constexpr (MODE != kModeMx) {
+      const float sbb = (MODE != 2) ? sBs[wn] : 1.0f;
+      sc0 = sAs[wm * 64 + l32] * sbb;
+      sc1 = sAs[wm * 64 + 32 + l32] * sbb;
+    }
 
     // LDS byte addresses of this lane's four swizzled 16-byte chunks in its A row and in its B
     // row of the current stage
@@ -247,7 +268,23 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
     if (kb + 1 < kb_end) issue_scales(kb + 1, stage ^ 1);
     const int64_t ko = (int64_t)kn * kBK;
     const uint32_t m0 = lds_addr(smem + (stage ^ 1) * kStageBytes) + (uint32_t)(wave * 32 * kBK);
-    if constexpr (MODE != 2) {
+    if constexpr (MODE == kModeMx) {
+      // the lane's E8M0 pairs: rows wm*64 + mi*32 + l32 of A, wn*128 + ni*32 + l32 of B, MX blocks
+      // 2h (first MFMA) and 2h + 1 (second) of the slice (mi, ni offsets are immediates)
+      const uint32_t xaj = sbase + (uint32_t)(kStageA + kStageB + (wm * 64 + l32) * 4 + 2 * h);
+      const uint32_t xbj = sbase + (uint32_t)(kStageA + kStageB + 1024 + (wn * 128 + l32) * 4 + 2 * h);
+      asm volatile(PURO_SLICE_ASM_MXSCALE
+                   : "+{v[0:15]}"(acc[0]), "+{v[16:31]}"(acc[1]), "+{v[32:47]}"(acc[2]), "+{v[48:63]}"(acc[3]),
+                     "+{v[64:79]}"(acc[4]), "+{v[80:95]}"(acc[5]), "+{v[96:111]}"(acc[6]), "+{v[112:127]}"(acc[7])
+                   : [aj0] "v"(arow + fcol[0]), [aj1] "v"(arow + fcol[1]), [aj2] "v"(arow + fcol[2]),
+                     [aj3] "v"(arow + fcol[3]), [bj0] "v"(brow + fcol[0]), [bj1] "v"(brow + fcol[1]),
+                     [bj2] "v"(brow + fcol[2]), [bj3] "v"(brow + fcol[3]), [xaj] "v"(xaj), [xbj] "v"(xbj),
+                     [ga0] "s"(a_grp[0] + ko), [ga1] "s"(a_grp[1] + ko), [ga2] "s"(a_grp[2] + ko),
+                     [ga3] "s"(a_grp[3] + ko), [gb0] "s"(b_grp[0] + ko), [gb1] "s"(b_grp[1] + ko),
+                     [gb2] "s"(b_grp[2] + ko), [gb3] "s"(b_grp[3] + ko), [oa0] "v"(a_off[0]), [oa1] "v"(a_off[1]),
+                     [ob0] "v"(b_off[0]), [ob1] "v"(b_off[1]), [m0] "s"(m0)
+                   : PURO_SLICE_ASM_MX_CLOBBERS, "m0", "memory");
+    } else if constexpr (MODE != 2) {
       asm volatile(PURO_SLICE_ASM_ROWSCALE
                    : "+{v[0:15]}"(acc[0]), "+{v[16:31]}"(acc[1]), "+{v[32:47]}"(acc[2]), "+{v[48:63]}"(acc[3]),
                      "+{v[64:79]}"(acc[4]), "+{v[80:95]}"(acc[5]), "+{v[96:111]}"(acc[6]), "+{v[112:127]}"(acc[7]),
@@ -282,7 +319,11 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
     // (the block ended with the slice's wait and barrier)
   }
 
-  if constexpr (MODE != 2)
+  if constexpr (MODE == kModeMx)
+    asm volatile(PURO_SLICE_ASM_MX_TAIL
+                 : "+{v[0:15]}"(acc[0]), "+{v[16:31]}"(acc[1]), "+{v[32:47]}"(acc[2]), "+{v[48:63]}"(acc[3]),
+                   "+{v[64:79]}"(acc[4]), "+{v[80:95]}"(acc[5]), "+{v[96:111]}"(acc[6]), "+{v[112:127]}"(acc[7]));
+  else if constexpr (MODE != 2)
     asm volatile(PURO_SLICE_ASM_ROWSCALE_TAIL : "+{v[112:127]}"(acc[7]) : "{v[144:159]}"(pcarry), [scp] "v"(scp));
   else
     asm volatile(PURO_SLICE_ASM_COLSCALE_TAIL : "+{v[112:127]}"(acc[7]), "+{v[144:159]}"(pcarry)
@@ -462,7 +503,8 @@ hipError_t launch_gemm(int mode, int64_t M, int64_t N, int64_t K, const uint8_t*
     switch (mode) {
       case 0: e = launch_one<0, false>(a, st); break;
       case 1: e = launch_one<1, false>(a, st); break;
-      default: e = launch_one<2, false>(a, st); break;
+      case 2: e = launch_one<2, false>(a, st); break;
+      default: e = launch_one<kModeMx, false>(a, st); break;
     }
     if (e != hipSuccess) return e;
     const int64_t work = M * (N / 4);
@@ -483,7 +525,9 @@ hipError_t launch_gemm(int mode, int64_t M, int64_t N, int64_t K, const uint8_t*
     case 2: return launch_one<1, false>(a, st);
     case 3: return launch_one<1, true>(a, st);
     case 4: return launch_one<2, false>(a, st);
-    default: return launch_one<2, true>(a, st);
+    case 5: return launch_one<2, true>(a, st);
+    case 6: return launch_one<kModeMx, false>(a, st);
+    default: return launch_one<kModeMx, true>(a, st);
   }
 }
 

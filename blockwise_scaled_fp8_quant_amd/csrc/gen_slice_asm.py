@@ -5,13 +5,21 @@
 
 The generated text is committed; the library build does not run this script.
 
-Two variants, differing in how the slice product of a tile is promoted:
+Three variants.  Two differ in how the slice product of a tile is promoted:
   ROWSCALE (FWD / DGRAD)  one scale per lane and row group: sA(i,kb) * sB(block,kb) is the
                           same for the 16 columns a lane owns (they sit in one 128x128
                           weight block), so the promotion is 16 FMAs:  C += P * sc.
   COLSCALE (WGRAD)        sB(j,kb) differs per column: 16 multiplies by the lane's 16 column
                           scales (read from LDS) and 16 FMAs by its row scale:
                           P *= sB(j);  C += P * sA(i).
+
+The third, MXSCALE (the MXFP8 GEMM), promotes nothing: every operand block of 32 elements
+carries an E8M0 scale that the scaled MFMA (v_mfma_scale_f32_32x32x64_f8f6f4) applies itself,
+so both MFMAs of a tile accumulate straight into the tile's accumulator.  In that instruction
+a scale block is the 16-byte group g of both lane halves, scaled by lane half g's scale byte
+(op_sel picks the byte); the kernel feeds lane half h chunks h, h+4 / h+2, h+6 so that these
+groups are the MX blocks 0, 2 / 1, 3 of the slice, and each lane's scale operand is one 16-bit
+LDS read holding MX blocks 2h (byte 0, first MFMA) and 2h + 1 (byte 1, second MFMA).
 
 Register map (per lane; pinned by the asm statement's constraints and clobbers):
   v[0:127]    accumulators: output tile T = 2*ni + mi (32 x 32, 16 fp32 per lane) in v[16T:16T+15]
@@ -23,11 +31,15 @@ Register map (per lane; pinned by the asm statement's constraints and clobbers):
   ROWSCALE:   v[192:207] B fragment buffer 0 (column tiles ni = 0, 2), v[208:223] buffer 1 (ni = 1, 3)
   COLSCALE:   v[192:207] B fragment (one buffer), v[208:223] the 16 column scales of the current
               column tile (column tile 3's are carried out of the block with tile 7's product)
+  MXSCALE:    v[192:223] as ROWSCALE; v128, v129 the A scale pairs of row groups 0 / 1,
+              v130 .. v133 the B scale pairs of column tiles 0 .. 3 (P registers are unused)
 Operands: %[aj0..3] / %[bj0..3] LDS byte addresses of this lane's 4 swizzled 16-byte chunks in
 its A / B row (row group / column tile offsets are 4096-byte immediates); ROWSCALE: %[sc0],
 %[sc1] the promotion scale of row group 0 / 1 for this slice, %[scp] the scale of the carried
 product; COLSCALE: %[sa0], %[sa1], %[sap] the row scales likewise and %[sbj] the LDS address
-of the lane's first column-scale quad (column tile / quad offsets are immediates); for the copy
+of the lane's first column-scale quad (column tile / quad offsets are immediates); MXSCALE:
+%[xaj] / %[xbj] the LDS addresses of the lane's A / B scale pair (row group / column tile
+offsets are immediates); for the copy
 of the next slice into the other LDS stage: %[ga0..3] / %[gb0..3] the (wave-uniform) global
 addresses of the wave's four 8-row groups of A / B at that slice, %[oa0], %[oa1] / %[ob0],
 %[ob1] the lane's byte offset within an even / odd group (row in group and swizzled chunk),
@@ -109,6 +121,22 @@ class Emitter:
         self.emit(f"v_mfma_f32_32x32x64_f8f6f4 v[{p}:{p + 15}], v[{b}:{b + 7}], v[{a}:{a + 7}], 0")
         self.emit(f"v_mfma_f32_32x32x64_f8f6f4 v[{p}:{p + 15}], v[{b + 8}:{b + 15}], v[{a + 8}:{a + 15}], v[{p}:{p + 15}]")
         self.produced[p] = self.ws
+
+    def mfma_pair_mx(self, acc, b, a, sb, sa):
+        """Two scaled MFMAs accumulating into acc: block byte 0 of the scale pairs, then byte 1."""
+        self.use(set(range(b, b + 16)) | set(range(a, a + 16)) | {sb, sa})
+        for half, sel in ((0, "op_sel:[0,0,0] op_sel_hi:[0,0,0]"), (8, "op_sel:[1,1,0] op_sel_hi:[0,0,0]")):
+            self.emit(f"v_mfma_scale_f32_32x32x64_f8f6f4 v[{acc}:{acc + 15}], v[{b + half}:{b + half + 7}], "
+                      f"v[{a + half}:{a + half + 7}], v[{acc}:{acc + 15}], v{sb}, v{sa} {sel}")
+        self.produced[acc] = self.ws
+
+    def read_u16(self, dst, addr, offset):
+        regs = {dst}
+        for p in self.pending:
+            assert not (p & regs), "LDS read overwrites a register of a pending read"
+        self.emit(f"ds_read_u16 v{dst}, %[{addr}] offset:{offset}")
+        self.pending.append(regs)
+        assert len(self.pending) <= 15, "more LDS reads in flight than lgkmcnt can count"
 
     def hazard(self, p):
         """Pad before the first VALU read of product buffer p (produced in this block)."""
@@ -206,6 +234,37 @@ def gen_colscale():
     return e.lines
 
 
+SA0, SB0 = 128, 130            # MXSCALE scale pairs: v128 + mi, v130 + ni
+
+
+def gen_mxscale():
+    e = Emitter()
+    e.read_u16(SA0, "xaj", 0)             # row group 0
+    e.read_u16(SB0, "xbj", 0)             # column tile 0
+    e.frag(BF0, "bj", 0)                  # B, column tile 0 -> buffer 0
+    e.frag(A0, "aj", 0)                   # A, row group 0
+    e.frag(A1, "aj", 4096)                # A, row group 1
+    e.wait_lgkm(4)                        # all but A1
+    for s in range(8):
+        ni, mi = s >> 1, s & 1
+        if s == 1:
+            e.wait_lgkm(7)                # A1 and the scales of row group 1 (newer: 3 scales, B(1))
+        elif mi == 0 and ni > 0:
+            e.wait_lgkm(0)                # B fragment and scales of column tile ni
+        e.mfma_pair_mx(16 * (2 * ni + mi), BF0 + 16 * (ni & 1), A0 + 16 * mi, SB0 + ni, SA0 + mi)
+        e.dma(s)
+        if s == 0:
+            e.read_u16(SA0 + 1, "xaj", 128)
+            for n in range(1, 4):
+                e.read_u16(SB0 + n, "xbj", 128 * n)
+        if mi == 0 and ni < 3:
+            e.frag(BF0 + 16 * ((ni + 1) & 1), "bj", (ni + 1) * 4096)
+    e.emit("s_waitcnt vmcnt(0) lgkmcnt(0)")
+    e.emit("s_barrier")
+    assert not e.pending
+    return e.lines
+
+
 def gen_tail(col):
     """After the last slice: promote the carried tile-7 product (padding kept for a block
     boundary the generator cannot see)."""
@@ -226,7 +285,7 @@ def macro(name, lines):
 
 
 def main():
-    row, col = gen_rowscale(), gen_colscale()
+    row, col, mxs = gen_rowscale(), gen_colscale(), gen_mxscale()
     here = os.path.dirname(os.path.abspath(__file__))
     with open(os.path.join(here, "gemm_slice_asm.inc"), "w") as f:
         f.write("// Generated by gen_slice_asm.py -- one 128-deep slice of the FP8 GEMM (see there).\n")
@@ -237,11 +296,18 @@ def main():
         f.write("// WGRAD: per-column scales from LDS times one row scale per lane and row group\n")
         f.write(macro("PURO_SLICE_ASM_COLSCALE", col))
         f.write(macro("PURO_SLICE_ASM_COLSCALE_TAIL", gen_tail(True)))
+        f.write("// MXFP8: E8M0 block scales applied by the scaled MFMA, no promotion\n")
+        f.write(macro("PURO_SLICE_ASM_MXSCALE", mxs))
+        f.write("// after the last slice: wait states between the last MFMA and the epilogue's reads\n")
+        e = Emitter()
+        e.nops(HAZARD_WAIT_STATES)
+        f.write(macro("PURO_SLICE_ASM_MX_TAIL", e.lines))
         f.write("// VGPRs the blocks use besides the pinned accumulators and the carried product (and, for\n"
                 "// COLSCALE, the carried column scales in v[208:223])\n")
         f.write("#define PURO_SLICE_ASM_CLOBBERS " + ", ".join(f'"v{r}"' for r in list(range(128, 144)) + list(range(160, 224))) + "\n")
         f.write("#define PURO_SLICE_ASM_COLSCALE_CLOBBERS " + ", ".join(f'"v{r}"' for r in list(range(128, 144)) + list(range(160, 208))) + "\n")
-    print(f"rowscale {len(row)} instructions, colscale {len(col)} instructions")
+        f.write("#define PURO_SLICE_ASM_MX_CLOBBERS " + ", ".join(f'"v{r}"' for r in list(range(128, 134)) + list(range(160, 224))) + "\n")
+    print(f"rowscale {len(row)}, colscale {len(col)}, mxscale {len(mxs)} instructions")
 
 
 if __name__ == "__main__":

@@ -14,12 +14,14 @@ hipError_t launch_quant_128x1(const void* x, int64_t T, int64_t C, int64_t ldx, 
                               int64_t ldqT, float* sT, hipStream_t st);
 hipError_t launch_quant_dual(const void* x, int64_t T, int64_t C, int64_t ldx, uint8_t* q, int64_t ldq,
                              float* s, uint8_t* qT, int64_t ldqT, float* sT, hipStream_t st);
+hipError_t launch_mx_quant_dual(const void* x, int64_t T, int64_t C, int64_t ldx, uint8_t* q, int64_t ldq,
+                                uint8_t* xs, uint8_t* qT, int64_t ldqT, uint8_t* xsT, hipStream_t st);
 hipError_t launch_quant_128x128(const void* w, int64_t N, int64_t K, int64_t ldw, uint8_t* q,
                                 int64_t ldq, float* s, uint8_t* qT, int64_t ldqT, float* sT,
                                 hipStream_t st);
 hipError_t launch_cast_e4m3(const float* v, int64_t n, uint8_t* q, hipStream_t st);
 
-// GEMM: mode 0 FWD, 1 DGRAD, 2 WGRAD; out_bf16 selects bf16 (else fp32) output; accumulate
+// GEMM: mode 0 FWD, 1 DGRAD, 2 WGRAD, 3 MXFP8 (E8M0 block scales, bytes [K/128][rows][4]); out_bf16 selects bf16 (else fp32) output; accumulate
 // (fp32 output only) adds the result to C.
 size_t gemm_workspace_bytes(int mode, int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm(int mode, int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,

@@ -289,6 +289,137 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(const uint16_t* __restr
 }
 
 // ---------------------------------------------------------------------------------------
+// MXFP8 dual quantizer (OCP Microscaling format with E4M3 elements; the pages' Blackwell
+// path): blocks of 32 elements along the contraction axis share one E8M0 scale
+// X = 2^(floor(log2 amax) - 8) (8: exponent of E4M3's largest normal, 448 = 1.75 * 2^8),
+// clamped to [2^-127, 2^127]; each element becomes E4M3_rne_sat(x / X).  Like the blockwise
+// dual kernel, one read of x [T, C] yields the row-wise codes (blocks along C, for FWD /
+// DGRAD) and the transposed column-wise codes (blocks along T, for WGRAD).  Scales are
+// written as bytes [C/128][T][4] and [T/128][C][4]: the four block scales of one 128-deep
+// slice of a row are adjacent.
+// Tile and thread layout as quant_dual_kernel (128 x 128, thread = 8 tokens x 8 columns):
+//   a row block (32 columns of one token) is one DPP quad of lanes: quad max;
+//   a column block (32 tokens of one column) is one wave's 4 thread rows: xor 16, 32.
+// The scale code is read off the amax's bf16 exponent field E: max(E - 8, 0), or 255 (NaN
+// scale) for a NaN or infinity.  x / X is the exact multiply by 2^(127 - code), built from
+// its exponent field; |x / X| < 512, clamped to +-448 before the convert (saturation).
+// Blocks with the NaN scale get NaN codes throughout.
+// ---------------------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t mx_code(uint32_t amax_bits) {
+  const uint32_t e = amax_bits >> 7;           // sign already cleared
+  return e == 255u ? 255u : (e > 8u ? e - 8u : 0u);
+}
+__device__ __forceinline__ float mx_mul(uint32_t code) {
+  return code == 255u ? __builtin_nanf("") : __uint_as_float((254u - code) << 23);
+}
+__device__ __forceinline__ float clamp448(float v) { return __builtin_amdgcn_fmed3f(v, -kE4M3Max, kE4M3Max); }
+
+__global__ __launch_bounds__(256) void mx_quant_dual_kernel(const uint16_t* __restrict__ x, int64_t T, int64_t C,
+                                                            int64_t ldx, uint8_t* __restrict__ q, int64_t ldq,
+                                                            uint8_t* __restrict__ xs, uint8_t* __restrict__ qT,
+                                                            int64_t ldqT, uint8_t* __restrict__ xsT, int bt) {
+  __shared__ uint8_t rowsc[128 * 4];       // [token][block]
+  __shared__ uint8_t colsc[128 * 4];       // [column][block]
+  __shared__ uint32_t stage[128 * 33];
+
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  const int tc = t & 15, tr = t >> 4;
+  int64_t tb, g;
+  tile_order(blockIdx.x, C / 128, bt, tb, g);
+  const int64_t tok0 = tb * 128 + tr * 8;
+  const int64_t col0 = g * 128 + tc * 8;
+
+  u32x4 v[8];
+  const uint16_t* xp = x + tok0 * ldx + col0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xp + i * ldx));
+
+  // row blocks: amax of tokens 2k (low half) / 2k+1 (high half) over the quad's 32 columns
+  uint32_t rcode[8];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    uint32_t m2[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const u32x4 w = v[2 * k + e];
+      m2[e] = hmax16(pk_max_u16(pk_max_u16(abs2(w.x), abs2(w.y)), pk_max_u16(abs2(w.z), abs2(w.w))));
+    }
+    uint32_t p = m2[0] | (m2[1] << 16);
+    p = pk_max_u16(p, dpp<kDppQuadXor1>(p));
+    p = pk_max_u16(p, dpp<kDppQuadXor2>(p));
+    rcode[2 * k] = mx_code(p & 0xFFFFu);
+    rcode[2 * k + 1] = mx_code(p >> 16);
+  }
+  // column blocks: amax of columns 8 tc + 2d (low) / + 1 (high) over the wave's 32 tokens
+  uint32_t ccode[8];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    uint32_t m = abs2(v[0][d]);
+#pragma unroll
+    for (int i = 1; i < 8; ++i) m = pk_max_u16(m, abs2(v[i][d]));
+    m = pk_max_u16(m, (uint32_t)__shfl_xor((int)m, 16));
+    m = pk_max_u16(m, (uint32_t)__shfl_xor((int)m, 32));
+    ccode[2 * d] = mx_code(m & 0xFFFFu);
+    ccode[2 * d + 1] = mx_code(m >> 16);
+  }
+  if ((tc & 3) == 0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) rowsc[(tr * 8 + i) * 4 + (tc >> 2)] = (uint8_t)rcode[i];
+  }
+  if (lane < 16) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) colsc[(tc * 8 + j) * 4 + wave] = (uint8_t)ccode[j];
+  }
+
+  // row-wise codes: token i's 8 columns -> 8 bytes
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float r = mx_mul(rcode[i]);
+    const u32x4 w = v[i];
+    u32x2 o;
+    o.x = cvt4(clamp448(bf16_lo(w.x) * r), clamp448(bf16_hi(w.x) * r), clamp448(bf16_lo(w.y) * r),
+               clamp448(bf16_hi(w.y) * r));
+    o.y = cvt4(clamp448(bf16_lo(w.z) * r), clamp448(bf16_hi(w.z) * r), clamp448(bf16_lo(w.w) * r),
+               clamp448(bf16_hi(w.w) * r));
+    if (rcode[i] == 255u) o |= 0x7F7F7F7Fu;
+    __builtin_nontemporal_store(o, reinterpret_cast<u32x2*>(q + (tok0 + i) * ldq + col0));
+  }
+  // column-wise codes: column j's 8 tokens -> two dwords of the staged transposed tile
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float r = mx_mul(ccode[j]);
+    float e[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t w = v[i][j >> 1];
+      e[i] = clamp448(((j & 1) ? bf16_hi(w) : bf16_lo(w)) * r);
+    }
+    uint32_t lo = cvt4(e[0], e[1], e[2], e[3]), hi = cvt4(e[4], e[5], e[6], e[7]);
+    if (ccode[j] == 255u) {
+      lo |= 0x7F7F7F7Fu;
+      hi |= 0x7F7F7F7Fu;
+    }
+    stage[(tc * 8 + j) * 33 + 2 * tr] = lo;
+    stage[(tc * 8 + j) * 33 + 2 * tr + 1] = hi;
+  }
+  __syncthreads();
+  if (t < 128)
+    reinterpret_cast<uint32_t*>(xs)[g * T + tb * 128 + t] = reinterpret_cast<const uint32_t*>(rowsc)[t];
+  else
+    reinterpret_cast<uint32_t*>(xsT)[tb * C + g * 128 + (t - 128)] = reinterpret_cast<const uint32_t*>(colsc)[t - 128];
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int cl = (t >> 3) + 32 * it;
+    const int part = t & 7;
+    const uint32_t* sp = stage + cl * 33 + part * 4;
+    const u32x4 o = {sp[0], sp[1], sp[2], sp[3]};
+    __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(qT + (g * 128 + cl) * ldqT + tb * 128 + part * 16));
+  }
+}
+
+// ---------------------------------------------------------------------------------------
 // 128x128 weight blocks.  One workgroup per block; thread t holds rows 8*(t>>4) .. +7 of
 // the block at columns 8*(t&15) .. +7 (8 coalesced 16-byte loads).  Block amax: packed
 // max in registers, DPP/cross-lane max in the wave, LDS across the 4 waves.  The thread's
@@ -410,6 +541,15 @@ hipError_t launch_quant_dual(const void* x, int64_t T, int64_t C, int64_t ldx, u
   if (nb * ng > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(quant_dual_kernel, dim3((unsigned)(nb * ng)), dim3(256), 0, st,
                      static_cast<const uint16_t*>(x), T, C, ldx, q, ldq, s, qT, ldqT, sT, token_run(nb));
+  return hipGetLastError();
+}
+
+hipError_t launch_mx_quant_dual(const void* x, int64_t T, int64_t C, int64_t ldx, uint8_t* q, int64_t ldq,
+                                uint8_t* xs, uint8_t* qT, int64_t ldqT, uint8_t* xsT, hipStream_t st) {
+  const int64_t nb = T / 128, ng = C / 128;
+  if (nb * ng > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(mx_quant_dual_kernel, dim3((unsigned)(nb * ng)), dim3(256), 0, st,
+                     static_cast<const uint16_t*>(x), T, C, ldx, q, ldq, xs, qT, ldqT, xsT, token_run(nb));
   return hipGetLastError();
 }
 

@@ -158,6 +158,49 @@ int puro_fp8_gemm_accumulate(int mode, int64_t M, int64_t N, int64_t K,
 size_t puro_fp8_gemm_workspace_size(int mode, int64_t M, int64_t N, int64_t K);
 
 /*
+ * MXFP8 variant.  On Blackwell the pages' linear layers run MXFP8 instead of the 1x128 /
+ * 128x128 scheme (agihunt digest, section 方法, FP8 bullet); the pages give no detail, so the
+ * format is the OCP Microscaling (MX) one with E4M3 elements:
+ *   - blocks of 32 consecutive elements along the consuming GEMM's contraction axis;
+ *   - one E8M0 scale byte per block, X = 2^(code - 127) (code 255 = NaN), chosen as
+ *     2^(floor(log2 amax) - 8) (8 = exponent of E4M3's largest normal, 448 = 1.75 * 2^8),
+ *     clamped to [2^-127, 2^127]; an all-zero block gets code 0;
+ *   - elements E4M3_rne_sat(x / X) (x / X is exact; values in [448, 512) X saturate).
+ *   - a block holding a NaN or an infinity gets code 255 and NaN element codes
+ *     (outside the bit-exact contract, as for the blockwise quantizers).
+ * Scale layout, for an operand [R, K] whose blocks run along K: bytes [K/128][R][4]; byte
+ * (kb, r, j) scales row r, elements 128 kb + 32 j .. 128 kb + 32 j + 31.
+ */
+
+/*
+ * MX dual quantizer: one read of x bf16 [T, C] yields
+ *   q  : codes [T, C] (row stride ldq), blocks along C; xs : scales [C/128][T][4];
+ *   qT : codes [C, T] (row stride ldqT), blocks along T; xsT: scales [T/128][C][4].
+ * Activations and gradients use both (FWD / DGRAD and WGRAD); for a weight W [Dout, Din],
+ * q serves FWD and qT (blocks along Dout) serves DGRAD.  T % 128 == 0, C % 128 == 0.
+ */
+int puro_fp8_mx_quant_dual(const void* x, int64_t T, int64_t C, int64_t ldx,
+                           uint8_t* q, int64_t ldq, uint8_t* xs,
+                           uint8_t* qT, int64_t ldqT, uint8_t* xsT, hipStream_t st);
+
+/*
+ * MX GEMM  C[M,N] = sum_k dec(A[i,k]) X_A(i, k/32) dec(B[j,k]) X_B(j, k/32), accumulated in fp32
+ * by the matrix cores, which apply the block scales themselves (no separate promotion).
+ *   A : codes [M, K] (row stride lda), xa: scales [K/128][M][4];
+ *   B : codes [N, K] (row stride ldb), xb: scales [K/128][N][4];
+ *   C, out_dtype, workspace: as puro_fp8_gemm (workspace from puro_fp8_mx_gemm_workspace_size).
+ * FWD / DGRAD / WGRAD differ only in which quantized tensors are passed.
+ */
+int puro_fp8_mx_gemm(int64_t M, int64_t N, int64_t K,
+                     const uint8_t* A, int64_t lda, const uint8_t* xa,
+                     const uint8_t* B, int64_t ldb, const uint8_t* xb,
+                     void* C, int64_t ldc, int out_dtype,
+                     void* workspace, size_t workspace_bytes, hipStream_t st);
+
+/* Bytes of workspace puro_fp8_mx_gemm needs for this problem (0 = none). */
+size_t puro_fp8_mx_gemm_workspace_size(int64_t M, int64_t N, int64_t K);
+
+/*
  * Verification helper: the device fp32 -> E4M3 cast every quantizer uses
  * (round-to-nearest-even, saturating at 448, sign kept, NaN -> NaN code), applied
  * elementwise: q[i] = E4M3(v[i]) for 0 <= i < n.  v and q must be 16-byte aligned.

@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_header_and_binding_agree():
     decl = declared_functions()
-    assert len(decl) == 10
+    assert len(decl) == 13
     assert sorted(P.EXPORTED_SYMBOLS) == decl
 
 
@@ -150,6 +150,37 @@ def test_gemm_accumulate_validation():
     need = P.puro_fp8_gemm_workspace_size(2, 2048, 2048, 16384)
     assert ga(M=2048, N=2048, K=16384, lda=16384, ldb=16384, ldc=2048) == WORKSPACE
     assert ga(M=2048, N=2048, K=16384, lda=16384, ldb=16384, ldc=2048, ws=A16, wsb=need - 1) == WORKSPACE
+
+
+def mq(x=A16, T=256, C=256, ldx=256, q=A16, ldq=256, xs=A16, qT=A16, ldqT=256, xsT=A16):
+    return P.lib.puro_fp8_mx_quant_dual(x, T, C, ldx, q, ldq, xs, qT, ldqT, xsT, None)
+
+
+def test_mx_quant_validation():
+    assert mq(T=0) == OK and mq(C=0) == OK
+    assert mq(T=64) == SHAPE and mq(C=96) == SHAPE and mq(T=-128) == SHAPE
+    for arg in ("x", "q", "xs", "qT", "xsT"):
+        assert mq(**{arg: None}) == NULLPTR, arg
+        assert mq(**{arg: MIS}) == ALIGN, arg
+    assert mq(ldx=128) == LD and mq(ldq=264) == LD and mq(ldqT=200) == LD
+
+
+def mg(M=256, N=256, K=256, A=A16, lda=256, xa=A16, B=A16, ldb=256, xb=A16, C=A16, ldc=256, dt=1, ws=None, wsb=0):
+    return P.lib.puro_fp8_mx_gemm(M, N, K, A, lda, xa, B, ldb, xb, C, ldc, dt, ws, wsb, None)
+
+
+def test_mx_gemm_validation():
+    assert mg(M=0) == OK and mg(N=0) == OK
+    assert mg(dt=3) == DTYPE
+    assert mg(K=100) == SHAPE and mg(M=-128) == SHAPE
+    assert mg(A=None) == NULLPTR and mg(xb=None) == NULLPTR and mg(C=None) == NULLPTR
+    assert mg(xa=MIS) == ALIGN and mg(B=MIS) == ALIGN
+    assert mg(lda=128) == LD and mg(ldc=100) == LD
+    need = P.puro_fp8_mx_gemm_workspace_size(2048, 2048, 16384)
+    assert need > 0
+    assert mg(M=2048, N=2048, K=16384, lda=16384, ldb=16384, ldc=2048) == WORKSPACE
+    # the internal MX mode is not a public puro_fp8_gemm mode
+    assert gm(mode=3) == MODE
 
 
 def test_cast_validation():

@@ -177,3 +177,56 @@ def test_gemm_full_size_sampled(P, wname, dout, din, mode):
     bound = TIGHT * den + (2.0 ** -8 * np.abs(ref) * (1 + 2.0 ** -7) if out_dtype == P.OUT_BF16 else 0.0)
     assert (diff <= bound).all()
     assert bool(t.isfinite(C).all())
+
+
+# --------------------------------------------------------------------------- MXFP8 variant
+
+@pytest.mark.parametrize("wname,dout,din", WEIGHTS)
+def test_mx_dual_quantizer_full_size_sampled(P, wname, dout, din):
+    from oracle import mx
+    t = torch()
+    for what, C, scale, seed in (("X", din, 1.0, 3), ("dY", dout, 1e-3, 4)):
+        say(f"[fullsize mx dual] {wname} {what} {TOKENS}x{C}")
+        x = student_t_bf16((TOKENS, C), seed * 100 + dout, scale)
+        q, xs, qT, xsT = P.puro_fp8_mx_quant_dual(x)
+        t.cuda.synchronize()
+        for tb in token_blocks(TOKENS, C + seed, n=2):
+            rows = slice(128 * tb, 128 * tb + 128)
+            xb = bits_of(x[rows])
+            rq, rxs = mx.quant_rows(xb)
+            rqT, rxsT = mx.quant_cols(xb)
+            assert_bytes_equal(host(q[rows]), rq, f"{what} MX rows of block {tb}")
+            assert_bytes_equal(host(xs[:, rows]), rxs, f"{what} MX row scales of block {tb}")
+            assert_bytes_equal(host(qT[:, rows]), rqT, f"{what} MX transposed codes of block {tb}")
+            assert_bytes_equal(host(xsT[tb:tb + 1]), rxsT, f"{what} MX column scales of block {tb}")
+
+
+@pytest.mark.parametrize("mode", ["FWD", "DGRAD", "WGRAD"])
+@pytest.mark.parametrize("wname,dout,din", WEIGHTS)
+def test_mx_gemm_full_size_sampled(P, wname, dout, din, mode):
+    from oracle import mx
+    t = torch()
+    M, N, K = {"FWD": (TOKENS, dout, din), "DGRAD": (TOKENS, din, dout), "WGRAD": (dout, din, TOKENS)}[mode]
+    out_dtype = P.OUT_FP32 if mode == "WGRAD" else P.OUT_BF16
+    say(f"[fullsize mx gemm] {wname} {mode} M,N,K={M},{N},{K}")
+    seed = 500 + 1000 * [w[0] for w in WEIGHTS].index(wname) + 10 * ["FWD", "DGRAD", "WGRAD"].index(mode)
+    A, B = e4m3_codes((M, K), seed), e4m3_codes((N, K), seed + 1)
+    g = gen(seed + 2)
+    xa = t.randint(115, 136, (K // 128, M, 4), generator=g, device="cuda", dtype=t.uint8)
+    xb = t.randint(115, 136, (K // 128, N, 4), generator=g, device="cuda", dtype=t.uint8)
+    C = P.puro_fp8_mx_gemm(A, xa, B, xb, out_dtype=out_dtype)
+    t.cuda.synchronize()
+    rng = np.random.default_rng(M + N + K + 1)
+    rows = np.sort(rng.choice(M, size=96, replace=False))
+    cols = np.sort(rng.choice(N, size=96, replace=False))
+    rt, ct = t.from_numpy(rows).cuda(), t.from_numpy(cols).cuda()
+    Ad = mx.dequant(host(A[rt]), host(xa[:, rt]))
+    Bd = mx.dequant(host(B[ct]), host(xb[:, ct]))
+    ref = Ad @ Bd.T
+    sub = host(C[rt][:, ct])
+    na, nb = np.sqrt((Ad * Ad).sum(1)), np.sqrt((Bd * Bd).sum(1))
+    err, diff, den = normalized_error(sub, ref, na, nb)
+    say(f"    max normalized error {err:.3e}")
+    rnd = 2.0 ** -8 * np.abs(ref) * (1 + 2.0 ** -7) if out_dtype == P.OUT_BF16 else 0.0
+    assert (diff <= TOL * den + rnd).all()
+    assert bool(t.isfinite(C).all())
