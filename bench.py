@@ -122,7 +122,7 @@ def summarize_pmc(fetch_dir: str, write_dir: str):
             op = op_of_kernel(n, last)
             if op is None or op == "copy":
                 continue
-            if op.startswith("gemm") and "gemm_kernel" in n:
+            if "gemm_kernel" in n:
                 last = op
             e = res.setdefault(op, {"FETCH_SIZE": 0.0, "WRITE_SIZE": 0.0, "launches": 0})
             e[counter] += v * 1024.0 * scale
@@ -268,7 +268,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=512)
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
