@@ -10,8 +10,9 @@ One step = one pass of the whole path over the full-layer workload at 16384 toke
 Inputs are seeded synthetic bf16 tensors already resident in HBM when timing starts.
 Prints ONE JSON line.  `value` = GEMM TFLOP/s of the whole step (all 12 GEMMs' flops
 divided by the step time, quantizers included in the time).  After the timed steps the
-standalone 1x128 and 128x1 quantizers are timed on the same tensors (reported under
-`kernels` with "in_step": false; not part of `value`), and so is the MXFP8 variant of the
+standalone 1x128 and 128x1 quantizers and the FWD GEMM with its output's 1x128 quantization
+fused into the epilogue are timed on the same tensors (reported under `kernels` with
+"in_step": false; not part of `value`), and so is the MXFP8 variant of the
 whole step (`mx_variant`: blocks of 32 with E8M0 scales; W, X and dY through the MX dual
 quantizer, then the three GEMMs).
 
@@ -69,7 +70,7 @@ def op_of_kernel(name: str, last_gemm):
     if "gemm_kernel<3" in name:
         return "mx_gemm"
     if "gemm_kernel<0" in name:
-        return "gemm_fwd"
+        return "gemm_fwd"          # (the fused-quant launches share the kernel; counted with FWD)
     if "gemm_kernel<1" in name:
         return "gemm_dgrad"
     if "gemm_kernel<2" in name:
@@ -222,7 +223,11 @@ def build_step(P, torch, d):
             ("mx_gemm_dgrad", lambda a=mGq, b=mGx, c=mWqT, e=mWxT, dX=dX: P.puro_fp8_mx_gemm(a, b, c, e, C=dX, out_dtype=P.OUT_BF16), gf(T, din, dout, 2), wname),
             ("mx_gemm_wgrad", lambda a=mGqT, b=mGxT, c=mXqT, e=mXxT, dW=dW: P.puro_fp8_mx_gemm(a, b, c, e, C=dW, out_dtype=P.OUT_FP32), gf(dout, din, T, 4), wname),
         ]
+        Yq, Ys = u8(T, dout), f32(dout // 128, T)
+        keep += [Yq, Ys]
         single += [
+            ("gemm_fwd_quant_out", lambda Xq=Xq, Xs=Xs, Wq=Wq, Ws=Ws, Y=Y, Yq=Yq, Ys=Ys:
+                P.puro_fp8_gemm_quant(P.FWD, Xq, Xs, Wq, Ws, C=Y, q=Yq, s=Ys), gf(T, dout, din, 2), wname),
             ("quant_act_1x128", lambda X=X, Xq=Xq, Xs=Xs: P.puro_fp8_quant_act_1x128(X, Xq, Xs), qb(T * din), wname),
             ("quant_act_1x128", lambda dY=dY, Gq=Gq, Gs=Gs: P.puro_fp8_quant_act_1x128(dY, Gq, Gs), qb(T * dout), wname),
             ("quant_act_128x1", lambda dY=dY, GqT=GqT, GsT=GsT: P.puro_fp8_quant_act_128x1(dY, GqT, GsT), qb(T * dout), wname),

@@ -18,7 +18,7 @@ __all__ = [
     "puro_fp8_quant_act_1x128", "puro_fp8_quant_act_128x1", "puro_fp8_quant_act_dual",
     "puro_fp8_quant_w_128x128", "puro_fp8_gemm", "puro_fp8_gemm_accumulate", "puro_fp8_gemm_workspace_size",
     "puro_fp8_cast_e4m3", "puro_fp8_strerror", "puro_fp8_version", "EXPORTED_SYMBOLS",
-    "puro_fp8_mx_quant_dual", "puro_fp8_mx_gemm", "puro_fp8_mx_gemm_workspace_size",
+    "puro_fp8_mx_quant_dual", "puro_fp8_mx_gemm", "puro_fp8_mx_gemm_workspace_size", "puro_fp8_gemm_quant",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpuro_fp8.so")
@@ -31,7 +31,7 @@ EXPORTED_SYMBOLS = (
     "puro_fp8_quant_act_1x128", "puro_fp8_quant_act_128x1", "puro_fp8_quant_act_dual", "puro_fp8_quant_w_128x128",
     "puro_fp8_gemm", "puro_fp8_gemm_accumulate", "puro_fp8_gemm_workspace_size", "puro_fp8_cast_e4m3",
     "puro_fp8_strerror", "puro_fp8_version",
-    "puro_fp8_mx_quant_dual", "puro_fp8_mx_gemm", "puro_fp8_mx_gemm_workspace_size",
+    "puro_fp8_mx_quant_dual", "puro_fp8_mx_gemm", "puro_fp8_mx_gemm_workspace_size", "puro_fp8_gemm_quant",
 )
 
 if not os.path.exists(LIB_PATH):
@@ -67,6 +67,7 @@ lib.puro_fp8_quant_act_dual.argtypes = [_p, _i64, _i64, _i64, _p, _i64, _p, _p, 
 lib.puro_fp8_quant_w_128x128.argtypes = [_p, _i64, _i64, _i64, _p, _i64, _p, _p, _i64, _p, _p]
 lib.puro_fp8_gemm.argtypes = [_int, _i64, _i64, _i64, _p, _i64, _p, _p, _i64, _p, _p, _i64, _int, _p, _sz, _p]
 lib.puro_fp8_gemm_accumulate.argtypes = [_int, _i64, _i64, _i64, _p, _i64, _p, _p, _i64, _p, _p, _i64, _p, _sz, _p]
+lib.puro_fp8_gemm_quant.argtypes = [_int, _i64, _i64, _i64, _p, _i64, _p, _p, _i64, _p, _p, _i64, _p, _i64, _p, _p, _sz, _p]
 lib.puro_fp8_mx_quant_dual.argtypes = [_p, _i64, _i64, _i64, _p, _i64, _p, _p, _i64, _p, _p]
 lib.puro_fp8_mx_gemm.argtypes = [_i64, _i64, _i64, _p, _i64, _p, _p, _i64, _p, _p, _i64, _int, _p, _sz, _p]
 lib.puro_fp8_mx_gemm_workspace_size.argtypes = [_i64, _i64, _i64]
@@ -203,6 +204,30 @@ def puro_fp8_gemm(mode, A, sA, B, sB, C=None, out_dtype: int = OUT_BF16, workspa
     _check(lib.puro_fp8_gemm(mode, M, N, K, _ptr(A), _ld(A), _ptr(sA), _ptr(B), _ld(B), _ptr(sB), _ptr(C), _ld(C),
                              out_dtype, _ptr(workspace), wbytes, _stream(stream)), "puro_fp8_gemm")
     return C
+
+
+def puro_fp8_gemm_quant(mode, A, sA, B, sB, C=None, q=None, s=None, workspace=None, stream=None):
+    """(C bf16 [M, N], q uint8 [M, N], s fp32 [N/128, M]): the GEMM and the 1x128 quantization of
+    its bf16 output along N, in one launch (two when the contraction is split)."""
+    torch = _torch()
+    if isinstance(mode, str):
+        mode = MODE_NAMES[mode]
+    M, K = A.shape
+    N = B.shape[0]
+    if C is None:
+        C = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    if q is None:
+        q = torch.empty((M, N), dtype=torch.uint8, device=A.device)
+    if s is None:
+        s = torch.empty((N // 128, M), dtype=torch.float32, device=A.device)
+    need = lib.puro_fp8_gemm_workspace_size(mode, M, N, K)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=A.device)
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.puro_fp8_gemm_quant(mode, M, N, K, _ptr(A), _ld(A), _ptr(sA), _ptr(B), _ld(B), _ptr(sB), _ptr(C),
+                                   _ld(C), _ptr(q), _ld(q), _ptr(s), _ptr(workspace), wbytes, _stream(stream)),
+           "puro_fp8_gemm_quant")
+    return C, q, s
 
 
 def puro_fp8_gemm_accumulate(mode, A, sA, B, sB, C, workspace=None, stream=None):

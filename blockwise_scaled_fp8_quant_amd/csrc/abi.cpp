@@ -76,7 +76,8 @@ int puro_fp8_quant_w_128x128(const void* w, int64_t N, int64_t K, int64_t ldw, u
 
 static int gemm_common(int mode, int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda, const float* sA,
                        const uint8_t* B, int64_t ldb, const float* sB, void* C, int64_t ldc, int out_dtype,
-                       bool accumulate, void* workspace, size_t workspace_bytes, hipStream_t st) {
+                       bool accumulate, void* workspace, size_t workspace_bytes, hipStream_t st,
+                       bool quant = false, uint8_t* q = nullptr, int64_t ldq = 0, float* qs = nullptr) {
   if (mode != PURO_GEMM_FWD && mode != PURO_GEMM_DGRAD && mode != PURO_GEMM_WGRAD && mode != kModeMx)
     return PURO_ERR_MODE;
   if (out_dtype != PURO_OUT_BF16 && out_dtype != PURO_OUT_FP32) return PURO_ERR_DTYPE;
@@ -87,6 +88,11 @@ static int gemm_common(int mode, int64_t M, int64_t N, int64_t K, const uint8_t*
   if (!C) return PURO_ERR_NULLPTR;
   if (!aligned16(C)) return PURO_ERR_ALIGN;
   if (ldc < N || (ldc * es) % 16) return PURO_ERR_LD;
+  if (quant) {
+    if (!q || !qs) return PURO_ERR_NULLPTR;
+    if (!aligned16(q) || !aligned16(qs)) return PURO_ERR_ALIGN;
+    if (ldq < N || ldq % 16) return PURO_ERR_LD;
+  }
   if (K > 0) {
     if (!A || !B || !sA || !sB) return PURO_ERR_NULLPTR;
     if (!aligned16(A) || !aligned16(B) || !aligned16(sA) || !aligned16(sB)) return PURO_ERR_ALIGN;
@@ -96,7 +102,7 @@ static int gemm_common(int mode, int64_t M, int64_t N, int64_t K, const uint8_t*
   const size_t need = puro::gemm_workspace_bytes(mode, M, N, K);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return PURO_ERR_WORKSPACE;
   return from_hip(puro::launch_gemm(mode, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, out_dtype == PURO_OUT_BF16,
-                                    accumulate, workspace, workspace_bytes, st));
+                                    accumulate, quant ? q : nullptr, ldq, qs, workspace, workspace_bytes, st));
 }
 
 int puro_fp8_gemm(int mode, int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda, const float* sA,
@@ -105,6 +111,14 @@ int puro_fp8_gemm(int mode, int64_t M, int64_t N, int64_t K, const uint8_t* A, i
   if (mode == kModeMx) return PURO_ERR_MODE;   // internal mode: puro_fp8_mx_gemm
   return gemm_common(mode, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, out_dtype, false, workspace, workspace_bytes,
                      st);
+}
+
+int puro_fp8_gemm_quant(int mode, int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda, const float* sA,
+                        const uint8_t* B, int64_t ldb, const float* sB, void* C, int64_t ldc, uint8_t* q, int64_t ldq,
+                        float* s, void* workspace, size_t workspace_bytes, hipStream_t st) {
+  if (mode == kModeMx) return PURO_ERR_MODE;
+  return gemm_common(mode, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, PURO_OUT_BF16, false, workspace, workspace_bytes,
+                     st, true, q, ldq, s);
 }
 
 int puro_fp8_mx_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda, const uint8_t* xa,

@@ -34,6 +34,7 @@
 
 #include <algorithm>
 
+#include "codec.hpp"
 #include "internal.hpp"
 #include "gemm_slice_asm.inc"
 
@@ -103,6 +104,9 @@ struct GemmArgs {
   void* C;
   int64_t ldc;
   int accumulate;        // fp32 output only: C = C + result (one fp32 add per element)
+  uint8_t* q;            // bf16 output only, optional: 1x128 quantization of C along N
+  int64_t ldq;
+  float* qs;             // its scales [N/128][M]
 };
 
 // Map the linear workgroup id to a (tile_m, tile_n) pair: XCD-contiguous, grouped rows.  The
@@ -343,8 +347,16 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
   static_assert(8 * 32 * kRow <= 2 * kStageBytes, "epilogue staging exceeds the LDS allocation");
   uint8_t* wbuf = smem + wave * (32 * kRow);
   const int rr = lane / kLanesPerRow, rc = lane % kLanesPerRow;
+  // 1x128 output quantization (bf16 output, optional): a wave's 128 columns are one group; the
+  // lane holds 64 of its row's values and lane ^ 32 the other 64.  The codes are staged per wave
+  // after the C staging area (8 x 32 x 272 + 8 x 32 x 144 bytes <= 2 x 66 KB).
+  constexpr int kQRow = 128 + 16;
+  static_assert(!OUT_BF16 || 8 * 32 * (kRow + kQRow) <= 2 * kStageBytes, "code staging exceeds the LDS allocation");
+  uint8_t* qbuf = smem + 8 * 32 * kRow + wave * (32 * kQRow);
+  const bool quant = OUT_BF16 && p.q != nullptr;
 #pragma unroll
   for (int mi = 0; mi < 2; ++mi) {
+    uint32_t am2 = 0;     // packed |bf16| max of this lane's 64 outputs of the row
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
@@ -355,14 +367,41 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
           o[0] = bf16x2_rne(acc[2 * ni + mi][4 * g + 0], acc[2 * ni + mi][4 * g + 1]);
           o[1] = bf16x2_rne(acc[2 * ni + mi][4 * g + 2], acc[2 * ni + mi][4 * g + 3]);
           *reinterpret_cast<g_u32x2*>(dst) = o;
+          am2 = pk_max_u16(am2, pk_max_u16(abs2(o[0]), abs2(o[1])));
         } else {
           const g_f32x4 o = {acc[2 * ni + mi][4 * g + 0], acc[2 * ni + mi][4 * g + 1],
                              acc[2 * ni + mi][4 * g + 2], acc[2 * ni + mi][4 * g + 3]};
           *reinterpret_cast<g_f32x4*>(dst) = o;
         }
       }
+    if (quant) {
+      // the same numerics as quant_1x128_kernel, applied to the bf16 values just written
+      uint32_t am = hmax16(am2);
+      am = umax(am, (uint32_t)__shfl_xor((int)am, 32));
+      float sc, r;
+      tile_scale(am, sc, r);
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const g_u32x2 o = *reinterpret_cast<const g_u32x2*>(wbuf + l32 * kRow + (ni * 32 + 8 * g + 4 * h) * kEs);
+          *reinterpret_cast<uint32_t*>(qbuf + l32 * kQRow + ni * 32 + 8 * g + 4 * h) =
+              cvt4(bf16_lo(o[0]) * r, bf16_hi(o[0]) * r, bf16_lo(o[1]) * r, bf16_hi(o[1]) * r);
+        }
+      if (h == 0 && rows_ok && cols_ok)
+        p.qs[(int64_t)((n0 >> 7) + wn) * p.M + m0 + wm * 64 + mi * 32 + l32] = sc;
+    }
     __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_wave_barrier();
+    if (quant && rows_ok && cols_ok) {
+      uint8_t* qrow = p.q + (int64_t)(m0 + wm * 64 + mi * 32) * p.ldq + n0 + wn * 128;
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        const int r = it * 8 + (lane >> 3), part = lane & 7;
+        *reinterpret_cast<g_u32x4*>(qrow + (int64_t)r * p.ldq + part * 16) =
+            *reinterpret_cast<const g_u32x4*>(qbuf + r * kQRow + part * 16);
+      }
+    }
     if (rows_ok && cols_ok) {
       uint8_t* cbase = static_cast<uint8_t*>(p.C) +
                        ((int64_t)split * p.split_stride + (int64_t)(m0 + wm * 64 + mi * 32) * p.ldc + n0 + wn * 128) * kEs;
@@ -471,11 +510,19 @@ static int choose_group(int64_t M, int64_t N, int64_t K) {
 
 hipError_t launch_gemm(int mode, int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
                        const float* sA, const uint8_t* B, int64_t ldb, const float* sB, void* C,
-                       int64_t ldc, bool out_bf16, bool accumulate, void* workspace, size_t workspace_bytes,
-                       hipStream_t st) {
+                       int64_t ldc, bool out_bf16, bool accumulate, uint8_t* q, int64_t ldq, float* qs,
+                       void* workspace, size_t workspace_bytes, hipStream_t st) {
   if (accumulate && out_bf16) return hipErrorInvalidValue;
+  if (q != nullptr && !out_bf16) return hipErrorInvalidValue;
   if (K == 0) {
     if (accumulate) return hipSuccess;   // C + 0
+    if (q != nullptr) {
+      const int64_t gy = M < 65535 ? M : 65535;
+      hipLaunchKernelGGL(zero_fill_kernel, dim3(8, (unsigned)gy), dim3(256), 0, st, C, M, N * 2, ldc * 2);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      return launch_quant_1x128(C, M, N, ldc, q, ldq, qs, st);
+    }
 
     const int64_t es = out_bf16 ? 2 : 4;
     const int64_t gy = M < 65535 ? M : 65535;
@@ -489,6 +536,7 @@ hipError_t launch_gemm(int mode, int64_t M, int64_t N, int64_t K, const uint8_t*
   if ((int64_t)a.tiles_m * a.tiles_n > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   a.A = A; a.lda = lda; a.sA = sA; a.B = B; a.ldb = ldb; a.sB = sB; a.C = C; a.ldc = ldc;
   a.accumulate = 0;
+  a.q = nullptr; a.ldq = 0; a.qs = nullptr;
   a.splits = choose_splits(M, N, K);
   a.group = choose_group(M, N, K);
   a.kb_per_split = (int)((K / kBK + a.splits - 1) / a.splits);
@@ -509,9 +557,15 @@ hipError_t launch_gemm(int mode, int64_t M, int64_t N, int64_t K, const uint8_t*
     if (e != hipSuccess) return e;
     const int64_t work = M * (N / 4);
     const int64_t blocks = std::min<int64_t>((work + 255) / 256, 4096);
-    if (out_bf16)
+    if (out_bf16) {
       hipLaunchKernelGGL(split_reduce_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, st,
                          static_cast<const float*>(workspace), a.splits, a.split_stride, (int)M, (int)N, C, ldc, 0);
+      if (q != nullptr) {   // quantize the reduced bf16 output: the same bytes as the fused epilogue
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        return launch_quant_1x128(C, M, N, ldc, q, ldq, qs, st);
+      }
+    }
     else
       hipLaunchKernelGGL(split_reduce_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, st,
                          static_cast<const float*>(workspace), a.splits, a.split_stride, (int)M, (int)N, C, ldc,
@@ -519,6 +573,7 @@ hipError_t launch_gemm(int mode, int64_t M, int64_t N, int64_t K, const uint8_t*
     return hipGetLastError();
   }
   a.accumulate = accumulate ? 1 : 0;
+  a.q = q; a.ldq = ldq; a.qs = qs;
   switch (mode * 2 + (out_bf16 ? 1 : 0)) {
     case 0: return launch_one<0, false>(a, st);
     case 1: return launch_one<0, true>(a, st);

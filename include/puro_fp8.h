@@ -154,7 +154,21 @@ int puro_fp8_gemm_accumulate(int mode, int64_t M, int64_t N, int64_t K,
                              float* C, int64_t ldc,
                              void* workspace, size_t workspace_bytes, hipStream_t st);
 
-/* Bytes of workspace puro_fp8_gemm and puro_fp8_gemm_accumulate need for this problem (0 = none). */
+/*
+ * GEMM with the 1x128 quantization of its output fused into the epilogue: C (bf16, as
+ * puro_fp8_gemm with PURO_OUT_BF16 writes it) and, from those bf16 values, exactly what
+ * puro_fp8_quant_act_1x128(C) would write: codes q [M, N] (row stride ldq bytes) and scales
+ * s [N/128][M].  For an output that feeds the next FP8 linear layer as its activation (groups
+ * of 128 along that layer's contraction axis, agihunt digest, section 方法, FP8 bullet), this
+ * saves re-reading C.  Arguments, layouts and errors as puro_fp8_gemm; q and s are required.
+ */
+int puro_fp8_gemm_quant(int mode, int64_t M, int64_t N, int64_t K,
+                        const uint8_t* A, int64_t lda, const float* sA,
+                        const uint8_t* B, int64_t ldb, const float* sB,
+                        void* C, int64_t ldc, uint8_t* q, int64_t ldq, float* s,
+                        void* workspace, size_t workspace_bytes, hipStream_t st);
+
+/* Bytes of workspace puro_fp8_gemm, puro_fp8_gemm_accumulate and puro_fp8_gemm_quant need (0 = none). */
 size_t puro_fp8_gemm_workspace_size(int mode, int64_t M, int64_t N, int64_t K);
 
 /*

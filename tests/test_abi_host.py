@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_header_and_binding_agree():
     decl = declared_functions()
-    assert len(decl) == 13
+    assert len(decl) == 14
     assert sorted(P.EXPORTED_SYMBOLS) == decl
 
 
@@ -181,6 +181,20 @@ def test_mx_gemm_validation():
     assert mg(M=2048, N=2048, K=16384, lda=16384, ldb=16384, ldc=2048) == WORKSPACE
     # the internal MX mode is not a public puro_fp8_gemm mode
     assert gm(mode=3) == MODE
+
+
+def gq(mode=0, M=256, N=256, K=256, A=A16, lda=256, sA=A16, B=A16, ldb=256, sB=A16, C=A16, ldc=256,
+       q=A16, ldq=256, s=A16, ws=None, wsb=0):
+    return P.lib.puro_fp8_gemm_quant(mode, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, q, ldq, s, ws, wsb, None)
+
+
+def test_gemm_quant_validation():
+    assert gq(M=0) == OK and gq(N=0) == OK
+    assert gq(mode=3) == MODE and gq(mode=7) == MODE
+    assert gq(N=100) == SHAPE
+    assert gq(q=None) == NULLPTR and gq(s=None) == NULLPTR and gq(C=None) == NULLPTR
+    assert gq(q=MIS) == ALIGN and gq(s=A16 + 4) == ALIGN
+    assert gq(ldq=128) == LD and gq(ldq=264) == LD and gq(ldc=260) == LD
 
 
 def test_cast_validation():
