@@ -423,22 +423,27 @@ __global__ __launch_bounds__(256) void mx_quant_dual_kernel(const uint16_t* __re
 // 128x128 weight blocks.  One workgroup per block; thread t holds rows 8*(t>>4) .. +7 of
 // the block at columns 8*(t&15) .. +7 (8 coalesced 16-byte loads).  Block amax: packed
 // max in registers, DPP/cross-lane max in the wave, LDS across the 4 waves.  The thread's
-// 8x8 sub-block is converted twice: row-wise for q and column-wise for the transposed
-// copy qT (8 consecutive rows of one column form the 8 bytes of a qT row segment).
+// 8x8 sub-block is converted row-wise for q (16 lanes write a row's 128 bytes) and
+// column-wise for the transposed copy qT, staged through LDS like the transposing activation
+// quantizers so that qT rows leave as 128-byte segments.  Workgroups take the blocks in runs
+// of consecutive N blocks of one K block (tile_order), so each qT row is written in long
+// contiguous runs.
 // ---------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void quant_128x128_kernel(const uint16_t* __restrict__ w, int64_t N,
                                                             int64_t K, int64_t ldw,
                                                             uint8_t* __restrict__ q, int64_t ldq,
                                                             float* __restrict__ s,
                                                             uint8_t* __restrict__ qT, int64_t ldqT,
-                                                            float* __restrict__ sT) {
+                                                            float* __restrict__ sT, int bt) {
   __shared__ uint32_t red[4];
+  __shared__ uint32_t stage[128 * 33];
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = t >> 6;
   const int cc = t & 15;
   const int rg = t >> 4;
-  const int64_t kb = blockIdx.x, nb = blockIdx.y;
+  int64_t nb, kb;
+  tile_order(blockIdx.x, K >> 7, bt, nb, kb);
   const int64_t n0 = nb * 128 + rg * 8;
   const int64_t k0 = kb * 128 + cc * 8;
 
@@ -464,30 +469,36 @@ __global__ __launch_bounds__(256) void quant_128x128_kernel(const uint16_t* __re
     if (sT) sT[kb * NB + nb] = sc;
   }
 
-  float f[8][8];
-#pragma unroll
-  for (int p = 0; p < 8; ++p) {
-    f[p][0] = bf16_lo(v[p].x) * r; f[p][1] = bf16_hi(v[p].x) * r;
-    f[p][2] = bf16_lo(v[p].y) * r; f[p][3] = bf16_hi(v[p].y) * r;
-    f[p][4] = bf16_lo(v[p].z) * r; f[p][5] = bf16_hi(v[p].z) * r;
-    f[p][6] = bf16_lo(v[p].w) * r; f[p][7] = bf16_hi(v[p].w) * r;
-  }
   uint8_t* qp = q + n0 * ldq + k0;
 #pragma unroll
   for (int p = 0; p < 8; ++p) {
+    const u32x4 x = v[p];
     u32x2 o;
-    o.x = cvt4(f[p][0], f[p][1], f[p][2], f[p][3]);
-    o.y = cvt4(f[p][4], f[p][5], f[p][6], f[p][7]);
+    o.x = cvt4(bf16_lo(x.x) * r, bf16_hi(x.x) * r, bf16_lo(x.y) * r, bf16_hi(x.y) * r);
+    o.y = cvt4(bf16_lo(x.z) * r, bf16_hi(x.z) * r, bf16_lo(x.w) * r, bf16_hi(x.w) * r);
     __builtin_nontemporal_store(o, reinterpret_cast<u32x2*>(qp + p * ldq));
   }
-  if (qT) {
-    uint8_t* tp = qT + k0 * ldqT + n0;
+  if (qT) {   // (uniform branch: qT is a kernel argument)
+    // column j of the thread's 8 columns: 8 rows -> two dwords of the staged [column][row quad] tile
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      u32x2 o;
-      o.x = cvt4(f[0][i], f[1][i], f[2][i], f[3][i]);
-      o.y = cvt4(f[4][i], f[5][i], f[6][i], f[7][i]);
-      __builtin_nontemporal_store(o, reinterpret_cast<u32x2*>(tp + i * ldqT));
+    for (int j = 0; j < 8; ++j) {
+      float e[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t x = v[i][j >> 1];
+        e[i] = ((j & 1) ? bf16_hi(x) : bf16_lo(x)) * r;
+      }
+      stage[(cc * 8 + j) * 33 + 2 * rg] = cvt4(e[0], e[1], e[2], e[3]);
+      stage[(cc * 8 + j) * 33 + 2 * rg + 1] = cvt4(e[4], e[5], e[6], e[7]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int cl = (t >> 3) + 32 * it;
+      const int part = t & 7;
+      const uint32_t* sp = stage + cl * 33 + part * 4;
+      const u32x4 o = {sp[0], sp[1], sp[2], sp[3]};
+      __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(qT + (kb * 128 + cl) * ldqT + nb * 128 + part * 16));
     }
   }
 }
@@ -556,10 +567,10 @@ hipError_t launch_mx_quant_dual(const void* x, int64_t T, int64_t C, int64_t ldx
 hipError_t launch_quant_128x128(const void* w, int64_t N, int64_t K, int64_t ldw, uint8_t* q,
                                 int64_t ldq, float* s, uint8_t* qT, int64_t ldqT, float* sT,
                                 hipStream_t st) {
-  const int64_t gx = K / 128, gy = N / 128;
-  if (gx > 0x7FFFFFFF || gy > 65535) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(quant_128x128_kernel, dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, st,
-                     static_cast<const uint16_t*>(w), N, K, ldw, q, ldq, s, qT, ldqT, sT);
+  const int64_t nb = N / 128, kb = K / 128;
+  if (nb * kb > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(quant_128x128_kernel, dim3((unsigned)(nb * kb)), dim3(256), 0, st,
+                     static_cast<const uint16_t*>(w), N, K, ldw, q, ldq, s, qT, ldqT, sT, token_run(nb));
   return hipGetLastError();
 }
 
