@@ -14,6 +14,10 @@ constexpr int kModeMx = 3;   // the MXFP8 GEMM's internal mode (not a public PUR
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// a * b > INT32_MAX for non-negative a, b (without overflowing): one workgroup per tile must fit a
+// one-dimensional grid
+inline bool too_many_blocks(int64_t a, int64_t b) { return a > 0 && b > kIntMax / a; }
+
 inline int from_hip(hipError_t e) {
   if (e == hipErrorInvalidConfiguration) return PURO_ERR_UNSUPPORTED;
   return e == hipSuccess ? PURO_OK : PURO_ERR_HIP;
@@ -43,7 +47,7 @@ int puro_fp8_quant_act_128x1(const void* x, int64_t T, int64_t C, int64_t ldx, u
   if (!x || !qT || !sT) return PURO_ERR_NULLPTR;
   if (!aligned16(x) || !aligned16(qT) || !aligned16(sT)) return PURO_ERR_ALIGN;
   if (ldx < C || ldqT < T || (ldx * 2) % 16 || ldqT % 16) return PURO_ERR_LD;
-  if (T / kGroup > 65535) return PURO_ERR_UNSUPPORTED;
+  if (too_many_blocks(T / kGroup, (C + 63) / 64)) return PURO_ERR_UNSUPPORTED;
   return from_hip(puro::launch_quant_128x1(x, T, C, ldx, qT, ldqT, sT, st));
 }
 
@@ -55,7 +59,7 @@ int puro_fp8_quant_act_dual(const void* x, int64_t T, int64_t C, int64_t ldx, ui
   if (!x || !q || !s || !qT || !sT) return PURO_ERR_NULLPTR;
   if (!aligned16(x) || !aligned16(q) || !aligned16(s) || !aligned16(qT) || !aligned16(sT)) return PURO_ERR_ALIGN;
   if (ldx < C || ldq < C || ldqT < T || (ldx * 2) % 16 || ldq % 16 || ldqT % 16) return PURO_ERR_LD;
-  if (T / kGroup > 65535) return PURO_ERR_UNSUPPORTED;
+  if (too_many_blocks(T / kGroup, C / kGroup)) return PURO_ERR_UNSUPPORTED;
   return from_hip(puro::launch_quant_dual(x, T, C, ldx, q, ldq, s, qT, ldqT, sT, st));
 }
 
@@ -70,7 +74,7 @@ int puro_fp8_quant_w_128x128(const void* w, int64_t N, int64_t K, int64_t ldw, u
   if (qT && (!aligned16(qT) || !aligned16(sT))) return PURO_ERR_ALIGN;
   if (ldw < K || ldq < K || (ldw * 2) % 16 || ldq % 16) return PURO_ERR_LD;
   if (qT && (ldqT < N || ldqT % 16)) return PURO_ERR_LD;
-  if (N / kGroup > 65535) return PURO_ERR_UNSUPPORTED;
+  if (too_many_blocks(N / kGroup, K / kGroup)) return PURO_ERR_UNSUPPORTED;
   return from_hip(puro::launch_quant_128x128(w, N, K, ldw, q, ldq, s, qT, ldqT, sT, st));
 }
 
@@ -140,6 +144,7 @@ int puro_fp8_mx_quant_dual(const void* x, int64_t T, int64_t C, int64_t ldx, uin
   if (!x || !q || !xs || !qT || !xsT) return PURO_ERR_NULLPTR;
   if (!aligned16(x) || !aligned16(q) || !aligned16(xs) || !aligned16(qT) || !aligned16(xsT)) return PURO_ERR_ALIGN;
   if (ldx < C || ldq < C || ldqT < T || (ldx * 2) % 16 || ldq % 16 || ldqT % 16) return PURO_ERR_LD;
+  if (too_many_blocks(T / kGroup, C / kGroup)) return PURO_ERR_UNSUPPORTED;
   return from_hip(puro::launch_mx_quant_dual(x, T, C, ldx, q, ldq, xs, qT, ldqT, xsT, st));
 }
 

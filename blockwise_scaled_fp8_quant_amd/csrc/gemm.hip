@@ -487,12 +487,18 @@ size_t gemm_workspace_bytes(int, int64_t M, int64_t N, int64_t K) {
 template <int MODE, bool BF16>
 static hipError_t launch_one(const GemmArgs& a, hipStream_t st) {
   const int smem = 2 * kStageBytes;
-  static bool attr_set = false;   // benign race: the attribute value is the same for every caller
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<MODE, BF16>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, smem);
+  // The dynamic-LDS limit is a per-device attribute of the kernel: set it once per device the
+  // caller launches on (benign race: every caller sets the same value).
+  constexpr int kMaxDevices = 64;
+  static bool attr_set[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices || !attr_set[dev]) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<MODE, BF16>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, smem);
     if (e != hipSuccess) return e;
-    attr_set = true;
+    if (dev >= 0 && dev < kMaxDevices) attr_set[dev] = true;
   }
   hipLaunchKernelGGL((gemm_kernel<MODE, BF16>), dim3(a.tiles_m * a.tiles_n * a.splits), dim3(kThreads), smem, st, a);
   return hipGetLastError();

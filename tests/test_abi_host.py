@@ -197,6 +197,15 @@ def test_gemm_quant_validation():
     assert gq(ldq=128) == LD and gq(ldq=264) == LD and gq(ldc=260) == LD
 
 
+def test_grid_limits_are_reported_not_launched():
+    # more than 2^31 - 1 tiles: refused on the host with UNSUPPORTED (nothing is launched)
+    T = 128 * (1 << 20)
+    C = 128 * 4096
+    assert qd(T=T, C=C, ldx=C, ldq=C, ldqT=T) == UNSUP
+    assert mq(T=T, C=C, ldx=C, ldq=C, ldqT=T) == UNSUP
+    assert q128x1(T=T, C=C, ldx=C, ldqT=T) == UNSUP
+
+
 def test_cast_validation():
     assert P.lib.puro_fp8_cast_e4m3(A16, 0, A16, None) == OK
     assert P.lib.puro_fp8_cast_e4m3(A16, -1, A16, None) == SHAPE
