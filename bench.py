@@ -69,8 +69,10 @@ def op_of_kernel(name: str, last_gemm):
         return "mx_quant_dual"
     if "gemm_kernel<3" in name:
         return "mx_gemm"
+    if "gemm_kernel<0, true, true>" in name:
+        return "gemm_fwd_quant_out"
     if "gemm_kernel<0" in name:
-        return "gemm_fwd"          # (the fused-quant launches share the kernel; counted with FWD)
+        return "gemm_fwd"
     if "gemm_kernel<1" in name:
         return "gemm_dgrad"
     if "gemm_kernel<2" in name:
@@ -313,11 +315,24 @@ def main():
             if events is not None:
                 events[i][1].record(stream)
 
-    def timed(op_list, iters):
-        """HIP events around every op of `iters` passes; returns (total ms, per-op stats)."""
+    def events(op_list, iters):
+        """Start/stop HIP events for every op of `iters` passes, each recorded once here so that
+        the device event exists before timing starts (torch creates it at the first record):
+        building them between the warm-up and the timed passes leaves the GPU idle long enough
+        for its clocks to drop, and the first timed steps then run slower."""
         ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in op_list]
               for _ in range(iters)]
         start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for e in [start, stop] + [x for row in ev for pair in row for x in pair]:
+            e.record(stream)
+        return start, stop, ev
+
+    def timed(op_list, iters, warmup):
+        """`warmup` untimed passes, then HIP events around every op of `iters` passes; returns
+        (total ms, per-op stats)."""
+        start, stop, ev = events(op_list, iters)
+        for _ in range(warmup):
+            run(op_list)
         torch.cuda.synchronize()
         start.record(stream)
         for k in range(iters):
@@ -355,23 +370,17 @@ def main():
             out[name] = row
         return out
 
-    for _ in range(args.warmup):
-        run(ops)
-    torch.cuda.synchronize()
-    log(f"warmup done ({args.warmup} steps); timing {args.steps} steps")
-    total_ms, per = timed(ops, args.steps)
+    log(f"{args.warmup} warm-up steps, then {args.steps} timed steps")
+    total_ms, per = timed(ops, args.steps, args.warmup)
     ms_per_step = total_ms / args.steps
     kernels = rows(per, total_ms, args.steps, True)
 
     # standalone single quantizers on the same tensors (outside the step)
-    run(single)
-    single_ms, single_per = timed(single, args.steps)
+    single_ms, single_per = timed(single, args.steps, 1)
     kernels.update(rows(single_per, single_ms, args.steps, False))
 
     # the MXFP8 variant of the step, timed the same way (not part of `value`)
-    for _ in range(args.warmup):
-        run(mxops)
-    mx_ms, mx_per = timed(mxops, args.steps)
+    mx_ms, mx_per = timed(mxops, args.steps, args.warmup)
     mx_step_ms = mx_ms / args.steps
     mx_variant = {"ms_per_step": round(mx_step_ms, 4),
                   "gemm_TFLOP/s_per_step": round(sum(w.get("flops", 0) for _, _, w, _ in mxops) / (mx_step_ms / 1e3) / 1e12, 2),

@@ -133,8 +133,11 @@ __device__ __forceinline__ void tile_of(int b, int tiles_m, int tiles_n, int gro
 // the 16 rows that one ds_read_b128 quarter-wave touches over all 64 banks.
 __device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 7); }
 
-template <int MODE, bool OUT_BF16>
+// QUANT: the epilogue also writes the 1x128 quantization of the bf16 output (a kernel of its own,
+// so that the plain GEMM carries none of it and profiles tell the two apart).
+template <int MODE, bool OUT_BF16, bool QUANT>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
+  static_assert(!QUANT || (OUT_BF16 && MODE != kModeMx), "output quantization needs a blockwise bf16 GEMM");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
   const int t = threadIdx.x;
@@ -351,30 +354,29 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
   // lane holds 64 of its row's values and lane ^ 32 the other 64.  The codes are staged per wave
   // after the C staging area (8 x 32 x 272 + 8 x 32 x 144 bytes <= 2 x 66 KB).
   constexpr int kQRow = 128 + 16;
-  static_assert(!OUT_BF16 || 8 * 32 * (kRow + kQRow) <= 2 * kStageBytes, "code staging exceeds the LDS allocation");
+  static_assert(!QUANT || 8 * 32 * (kRow + kQRow) <= 2 * kStageBytes, "code staging exceeds the LDS allocation");
   uint8_t* qbuf = smem + 8 * 32 * kRow + wave * (32 * kQRow);
-  const bool quant = OUT_BF16 && p.q != nullptr;
 #pragma unroll
   for (int mi = 0; mi < 2; ++mi) {
-    uint32_t am2 = 0;     // packed |bf16| max of this lane's 64 outputs of the row
+    [[maybe_unused]] uint32_t am2 = 0;     // packed |bf16| max of this lane's 64 outputs of the row
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         uint8_t* dst = wbuf + l32 * kRow + (ni * 32 + 8 * g + 4 * h) * kEs;
-        if (OUT_BF16) {
+        if constexpr (OUT_BF16) {
           g_u32x2 o;
           o[0] = bf16x2_rne(acc[2 * ni + mi][4 * g + 0], acc[2 * ni + mi][4 * g + 1]);
           o[1] = bf16x2_rne(acc[2 * ni + mi][4 * g + 2], acc[2 * ni + mi][4 * g + 3]);
           *reinterpret_cast<g_u32x2*>(dst) = o;
-          am2 = pk_max_u16(am2, pk_max_u16(abs2(o[0]), abs2(o[1])));
+          if constexpr (QUANT) am2 = pk_max_u16(am2, pk_max_u16(abs2(o[0]), abs2(o[1])));
         } else {
           const g_f32x4 o = {acc[2 * ni + mi][4 * g + 0], acc[2 * ni + mi][4 * g + 1],
                              acc[2 * ni + mi][4 * g + 2], acc[2 * ni + mi][4 * g + 3]};
           *reinterpret_cast<g_f32x4*>(dst) = o;
         }
       }
-    if (quant) {
+    if constexpr (QUANT) {
       // the same numerics as quant_1x128_kernel, applied to the bf16 values just written
       uint32_t am = hmax16(am2);
       am = umax(am, (uint32_t)__shfl_xor((int)am, 32));
@@ -393,7 +395,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
     }
     __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_wave_barrier();
-    if (quant && rows_ok && cols_ok) {
+    if (QUANT && rows_ok && cols_ok) {
       uint8_t* qrow = p.q + (int64_t)(m0 + wm * 64 + mi * 32) * p.ldq + n0 + wn * 128;
 #pragma unroll
       for (int it = 0; it < 4; ++it) {
@@ -484,7 +486,7 @@ size_t gemm_workspace_bytes(int, int64_t M, int64_t N, int64_t K) {
   return sp > 1 ? (size_t)sp * (size_t)M * (size_t)N * 4 : 0;
 }
 
-template <int MODE, bool BF16>
+template <int MODE, bool BF16, bool QUANT = false>
 static hipError_t launch_one(const GemmArgs& a, hipStream_t st) {
   const int smem = 2 * kStageBytes;
   // The dynamic-LDS limit is a per-device attribute of the kernel: set it once per device the
@@ -495,12 +497,12 @@ static hipError_t launch_one(const GemmArgs& a, hipStream_t st) {
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= kMaxDevices || !attr_set[dev]) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<MODE, BF16>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<MODE, BF16, QUANT>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, smem);
     if (e != hipSuccess) return e;
     if (dev >= 0 && dev < kMaxDevices) attr_set[dev] = true;
   }
-  hipLaunchKernelGGL((gemm_kernel<MODE, BF16>), dim3(a.tiles_m * a.tiles_n * a.splits), dim3(kThreads), smem, st, a);
+  hipLaunchKernelGGL((gemm_kernel<MODE, BF16, QUANT>), dim3(a.tiles_m * a.tiles_n * a.splits), dim3(kThreads), smem, st, a);
   return hipGetLastError();
 }
 
@@ -580,6 +582,14 @@ hipError_t launch_gemm(int mode, int64_t M, int64_t N, int64_t K, const uint8_t*
   }
   a.accumulate = accumulate ? 1 : 0;
   a.q = q; a.ldq = ldq; a.qs = qs;
+  if (q != nullptr) {
+    switch (mode) {
+      case 0: return launch_one<0, true, true>(a, st);
+      case 1: return launch_one<1, true, true>(a, st);
+      case 2: return launch_one<2, true, true>(a, st);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (mode * 2 + (out_bf16 ? 1 : 0)) {
     case 0: return launch_one<0, false>(a, st);
     case 1: return launch_one<0, true>(a, st);
