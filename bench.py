@@ -9,7 +9,10 @@ One step = one pass of the whole path over the full-layer workload at 16384 toke
                                                                 WGRAD dW = dY^T X  (fp32 out)
 Inputs are seeded synthetic bf16 tensors already resident in HBM when timing starts.
 Prints ONE JSON line.  `value` = GEMM TFLOP/s of the whole step (all 12 GEMMs' flops
-divided by the step time, quantizers included in the time).  After the timed steps the
+divided by the step time, quantizers included in the time), timed with HIP events around the
+K steps only.  The per-kernel durations (`kernels`, `roofline`) come from K more steps right
+after, with an event pair around every launch (these add idle time between kernels, so that
+pass's step time, `ms_per_step_instrumented`, is longer).  After the timed steps the
 standalone 1x128 and 128x1 quantizers and the FWD GEMM with its output's 1x128 quantization
 fused into the epilogue are timed on the same tensors (reported under `kernels` with
 "in_step": false; not part of `value`), and so is the MXFP8 variant of the
@@ -315,12 +318,12 @@ def main():
             if events is not None:
                 events[i][1].record(stream)
 
-    def events(op_list, iters):
+    def events(n_ops, iters):
         """Start/stop HIP events for every op of `iters` passes, each recorded once here so that
         the device event exists before timing starts (torch creates it at the first record):
         building them between the warm-up and the timed passes leaves the GPU idle long enough
         for its clocks to drop, and the first timed steps then run slower."""
-        ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in op_list]
+        ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in range(n_ops)]
               for _ in range(iters)]
         start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         for e in [start, stop] + [x for row in ev for pair in row for x in pair]:
@@ -328,16 +331,24 @@ def main():
         return start, stop, ev
 
     def timed(op_list, iters, warmup):
-        """`warmup` untimed passes, then HIP events around every op of `iters` passes; returns
-        (total ms, per-op stats)."""
-        start, stop, ev = events(op_list, iters)
+        """`warmup` untimed passes; `iters` timed passes with HIP events only around the whole
+        run (the step time: an event pair around every op adds ~7 us of idle GPU per op); then
+        `iters` more passes with an event pair around every op, for the per-kernel durations.
+        Returns (ms of the uninstrumented passes, ms of the instrumented ones, per-op stats)."""
+        start, stop, _ = events(0, 0)
+        start2, stop2, ev = events(len(op_list), iters)
         for _ in range(warmup):
             run(op_list)
         torch.cuda.synchronize()
         start.record(stream)
+        for _ in range(iters):
+            run(op_list)
+        stop.record(stream)
+        torch.cuda.synchronize()
+        start2.record(stream)
         for k in range(iters):
             run(op_list, ev[k])
-        stop.record(stream)
+        stop2.record(stream)
         torch.cuda.synchronize()
         per = {}
         for k in range(iters):
@@ -347,7 +358,7 @@ def main():
                 e["launches"] += 1
                 e["flops"] += work.get("flops", 0)
                 e["bytes"] += work.get("bytes", 0)
-        return start.elapsed_time(stop), per
+        return start.elapsed_time(stop), start2.elapsed_time(stop2), per
 
     hbm = load_traffic()
 
@@ -371,20 +382,21 @@ def main():
         return out
 
     log(f"{args.warmup} warm-up steps, then {args.steps} timed steps")
-    total_ms, per = timed(ops, args.steps, args.warmup)
+    total_ms, inst_ms, per = timed(ops, args.steps, args.warmup)
     ms_per_step = total_ms / args.steps
-    kernels = rows(per, total_ms, args.steps, True)
+    kernels = rows(per, inst_ms, args.steps, True)
 
     # standalone single quantizers on the same tensors (outside the step)
-    single_ms, single_per = timed(single, args.steps, 1)
+    _, single_ms, single_per = timed(single, args.steps, 1)
     kernels.update(rows(single_per, single_ms, args.steps, False))
 
     # the MXFP8 variant of the step, timed the same way (not part of `value`)
-    mx_ms, mx_per = timed(mxops, args.steps, args.warmup)
+    mx_ms, mx_inst_ms, mx_per = timed(mxops, args.steps, args.warmup)
     mx_step_ms = mx_ms / args.steps
     mx_variant = {"ms_per_step": round(mx_step_ms, 4),
                   "gemm_TFLOP/s_per_step": round(sum(w.get("flops", 0) for _, _, w, _ in mxops) / (mx_step_ms / 1e3) / 1e12, 2),
-                  "kernels": rows(mx_per, mx_ms, args.steps, True)}
+                  "ms_per_step_instrumented": round(mx_inst_ms / args.steps, 4),
+                  "kernels": rows(mx_per, mx_inst_ms, args.steps, True)}
 
     gemm_flops = sum(w.get("flops", 0) for _, _, w, _ in ops)
     value = gemm_flops / (ms_per_step / 1e3) / 1e12
@@ -413,7 +425,8 @@ def main():
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step_instrumented": round(inst_ms / args.steps, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "fp8e4m3xfp8e4m3->fp32", "data": "synthetic",
         "config": {"workload": "layer_sweep: 16384 tokens, seed 0, weights qkv 4096x2048, o 2048x2048, "
                                "gate_up 12288x2048, down 2048x6144; per weight: W 128x128 (+T), X and dY dual "
