@@ -66,7 +66,7 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def op_of_kernel(name: str, last_gemm):
+def op_of_kernel(name: str):
     """Map a dispatched kernel's name to the bench op it belongs to (None: not a path kernel)."""
     if "mx_quant_dual" in name:
         return "mx_quant_dual"
@@ -80,8 +80,6 @@ def op_of_kernel(name: str, last_gemm):
         return "gemm_dgrad"
     if "gemm_kernel<2" in name:
         return "gemm_wgrad"
-    if "split_reduce" in name or "zero_fill" in name:
-        return last_gemm
     if "quant_dual" in name:
         return "quant_act_dual"
     if "quant_1x128" in name:
@@ -118,21 +116,21 @@ def summarize_pmc(fetch_dir: str, write_dir: str):
     factors = {}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows = read_counter_csv(d, counter)
-        copies = [v for n, v in rows if op_of_kernel(n, None) == "copy"]
+        copies = [v for n, v in rows if op_of_kernel(n) == "copy"]
         if not copies:
             raise SystemExit(f"{counter}: the calibration copy was not found")
         factors[counter] = (COPY_BYTES, copies[0] * 1024.0)
         scale = COPY_BYTES / (copies[0] * 1024.0)
-        last = None
+        last = None        # a split GEMM's reduce kernel runs right after the GEMM kernel
         for n, v in rows:
-            op = op_of_kernel(n, last)
+            op = last if "split_reduce" in n else op_of_kernel(n)
             if op is None or op == "copy":
                 continue
             if "gemm_kernel" in n:
                 last = op
             e = res.setdefault(op, {"FETCH_SIZE": 0.0, "WRITE_SIZE": 0.0, "launches": 0})
             e[counter] += v * 1024.0 * scale
-            if counter == "FETCH_SIZE" and "split_reduce" not in n and "zero_fill" not in n:
+            if counter == "FETCH_SIZE" and "split_reduce" not in n:
                 e["launches"] += 1
     lines = ["# HBM traffic per launch: layer sweep, 16384 tokens, seed 0 (bench step)",
              "# rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o pmc -- python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline",
