@@ -290,7 +290,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
                      [ga3] "s"(a_grp[3] + ko), [gb0] "s"(b_grp[0] + ko), [gb1] "s"(b_grp[1] + ko),
                      [gb2] "s"(b_grp[2] + ko), [gb3] "s"(b_grp[3] + ko), [oa0] "v"(a_off[0]), [oa1] "v"(a_off[1]),
                      [ob0] "v"(b_off[0]), [ob1] "v"(b_off[1]), [m0] "s"(m0)
-                   : PURO_SLICE_ASM_MX_CLOBBERS, "m0", "memory");
+                   : PURO_SLICE_ASM_MX_CLOBBERS, "m0", "scc", "memory");
     } else if constexpr (MODE != 2) {
       asm volatile(PURO_SLICE_ASM_ROWSCALE
                    : "+{v[0:15]}"(acc[0]), "+{v[16:31]}"(acc[1]), "+{v[32:47]}"(acc[2]), "+{v[48:63]}"(acc[3]),
@@ -304,7 +304,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
                      [ga3] "s"(a_grp[3] + ko), [gb0] "s"(b_grp[0] + ko), [gb1] "s"(b_grp[1] + ko),
                      [gb2] "s"(b_grp[2] + ko), [gb3] "s"(b_grp[3] + ko), [oa0] "v"(a_off[0]), [oa1] "v"(a_off[1]),
                      [ob0] "v"(b_off[0]), [ob1] "v"(b_off[1]), [m0] "s"(m0)
-                   : PURO_SLICE_ASM_CLOBBERS, "m0", "memory");
+                   : PURO_SLICE_ASM_CLOBBERS, "m0", "scc", "memory");
     } else {
       // the lane's column scales: columns wn*128 + ni*32 + 8g + 4h .. +3 (ni, g immediates)
       const uint32_t sbj = sbase + (uint32_t)(kStageA + kStageB + 1024 + (wn * 128 + 4 * h) * 4);
@@ -320,7 +320,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
                      [ga3] "s"(a_grp[3] + ko), [gb0] "s"(b_grp[0] + ko), [gb1] "s"(b_grp[1] + ko),
                      [gb2] "s"(b_grp[2] + ko), [gb3] "s"(b_grp[3] + ko), [oa0] "v"(a_off[0]), [oa1] "v"(a_off[1]),
                      [ob0] "v"(b_off[0]), [ob1] "v"(b_off[1]), [m0] "s"(m0)
-                   : PURO_SLICE_ASM_COLSCALE_CLOBBERS, "m0", "memory");
+                   : PURO_SLICE_ASM_COLSCALE_CLOBBERS, "m0", "scc", "memory");
     }
     scp = sc1;  // tile 7's product stays in pcarry until the next block (or the tail)
     // (the block ended with the slice's wait and barrier)
