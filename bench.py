@@ -25,9 +25,9 @@ HBM traffic of each kernel comes from two rocprofv3 counter runs of this script 
 then WRITE_SIZE), both scaled by what the same counter reads for a plain copy of known size
 that every run performs once, untimed, before the steps:
 
-    rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o pmc -- python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline
-    rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o pmc -- python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline
-    python bench.py --summarize-pmc gpurun_out/pmc_fetch gpurun_out/pmc_write   # writes TRAFFIC_FILE
+    rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/pmc_fetch -o pmc -- python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline
+    rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/pmc_write -o pmc -- python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline
+    python bench.py --summarize-pmc OUT/pmc_fetch OUT/pmc_write   # writes TRAFFIC_FILE
 
 The summary records a hash of the kernel sources; once they change, `traffic` reads null
 until the counters are taken again.
@@ -133,9 +133,9 @@ def summarize_pmc(fetch_dir: str, write_dir: str):
             if counter == "FETCH_SIZE" and "split_reduce" not in n:
                 e["launches"] += 1
     lines = ["# HBM traffic per launch: layer sweep, 16384 tokens, seed 0 (bench step)",
-             "# rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o pmc -- python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline",
-             "# rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o pmc -- python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline",
-             "# python bench.py --summarize-pmc gpurun_out/pmc_fetch gpurun_out/pmc_write",
+             "# rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/pmc_fetch -o pmc -- python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline",
+             "# rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/pmc_write -o pmc -- python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline",
+             "# python bench.py --summarize-pmc OUT/pmc_fetch OUT/pmc_write   (OUT: the counter runs' output directory)",
              "# counters are scaled so that the calibration copy (256 MiB read + 256 MiB written) reads its own size;",
              "# a GEMM op includes its split-K reduce kernel",
              f"kernel_source_hash {kernel_source_hash()}"]
