@@ -98,6 +98,8 @@ struct GemmArgs {
   const uint8_t* A;
   int64_t lda;
   const float* sA;
+  int64_t ldsa;          // elements (MX: 4-byte rows) between consecutive slices of sA: M, or the
+                         // full problem's M when this launch covers a range of its rows
   const uint8_t* B;
   int64_t ldb;
   const float* sB;
@@ -193,11 +195,11 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
       // E8M0 tiles: [K/128][rows][4] bytes; 256 rows x 4 bytes = 1 KB per operand per slice
       const uint8_t* xa = reinterpret_cast<const uint8_t*>(p.sA);
       const uint8_t* xb = reinterpret_cast<const uint8_t*>(p.sB);
-      if (wave == 0) g2lds16(xa + ((int64_t)kb * p.M + s_m) * 4, st + kStageA + kStageB);
+      if (wave == 0) g2lds16(xa + ((int64_t)kb * p.ldsa + s_m) * 4, st + kStageA + kStageB);
       if (wave == 1) g2lds16(xb + ((int64_t)kb * p.N + s_n) * 4, st + kStageA + kStageB + 1024);
       return;
     }
-    if (wave == 0) g2lds16(p.sA + (int64_t)kb * p.M + s_m, st + kStageA + kStageB);
+    if (wave == 0) g2lds16(p.sA + (int64_t)kb * p.ldsa + s_m, st + kStageA + kStageB);
     if (wave == 1) {
       if (MODE == 2)
         g2lds16(p.sB + (int64_t)kb * p.N + s_n, st + kStageA + kStageB + 1024);
@@ -516,33 +518,18 @@ static int choose_group(int64_t M, int64_t N, int64_t K) {
   return K <= 2048 ? 4 : 8;
 }
 
-hipError_t launch_gemm(int mode, int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
-                       const float* sA, const uint8_t* B, int64_t ldb, const float* sB, void* C,
-                       int64_t ldc, bool out_bf16, bool accumulate, uint8_t* q, int64_t ldq, float* qs,
-                       void* workspace, size_t workspace_bytes, hipStream_t st) {
-  if (accumulate && out_bf16) return hipErrorInvalidValue;
-  if (q != nullptr && !out_bf16) return hipErrorInvalidValue;
-  if (K == 0) {
-    if (accumulate) return hipSuccess;   // C + 0
-    if (q != nullptr) {
-      const int64_t gy = M < 65535 ? M : 65535;
-      hipLaunchKernelGGL(zero_fill_kernel, dim3(8, (unsigned)gy), dim3(256), 0, st, C, M, N * 2, ldc * 2);
-      const hipError_t e = hipGetLastError();
-      if (e != hipSuccess) return e;
-      return launch_quant_1x128(C, M, N, ldc, q, ldq, qs, st);
-    }
-
-    const int64_t es = out_bf16 ? 2 : 4;
-    const int64_t gy = M < 65535 ? M : 65535;
-    hipLaunchKernelGGL(zero_fill_kernel, dim3(8, (unsigned)gy), dim3(256), 0, st, C, M, N * es, ldc * es);
-    return hipGetLastError();
-  }
+// One GEMM launch (and its split-K reduce) over M rows of A and C; the slices of sA are ldsa
+// apart (ldsa >= M).
+static hipError_t launch_rows(int mode, int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
+                              const float* sA, int64_t ldsa, const uint8_t* B, int64_t ldb, const float* sB,
+                              void* C, int64_t ldc, bool out_bf16, bool accumulate, uint8_t* q, int64_t ldq,
+                              float* qs, void* workspace, size_t workspace_bytes, hipStream_t st) {
   GemmArgs a;
   a.M = (int)M; a.N = (int)N; a.K = (int)K;
   a.tiles_m = (int)((M + kBM - 1) / kBM);
   a.tiles_n = (int)((N + kBN - 1) / kBN);
   if ((int64_t)a.tiles_m * a.tiles_n > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  a.A = A; a.lda = lda; a.sA = sA; a.B = B; a.ldb = ldb; a.sB = sB; a.C = C; a.ldc = ldc;
+  a.A = A; a.lda = lda; a.sA = sA; a.ldsa = ldsa; a.B = B; a.ldb = ldb; a.sB = sB; a.C = C; a.ldc = ldc;
   a.accumulate = 0;
   a.q = nullptr; a.ldq = 0; a.qs = nullptr;
   a.splits = choose_splits(M, N, K);
@@ -551,7 +538,7 @@ hipError_t launch_gemm(int mode, int64_t M, int64_t N, int64_t K, const uint8_t*
   a.split_stride = 0;
   if (a.splits > 1) {
     // partial sums (fp32, [split][M][N]) in the caller's workspace, then one reduction
-    if (workspace == nullptr || workspace_bytes < gemm_workspace_bytes(mode, M, N, K)) return hipErrorInvalidValue;
+    if (workspace == nullptr || workspace_bytes < (size_t)a.splits * (size_t)M * (size_t)N * 4) return hipErrorInvalidValue;
     a.C = workspace;
     a.ldc = N;
     a.split_stride = M * N;
@@ -600,6 +587,61 @@ hipError_t launch_gemm(int mode, int64_t M, int64_t N, int64_t K, const uint8_t*
     case 6: return launch_one<kModeMx, false>(a, st);
     default: return launch_one<kModeMx, true>(a, st);
   }
+}
+
+// Rows of a leading part that runs without a contraction split, when the whole problem would be
+// split only to fill its last, partial wave of tiles: the whole waves first (as whole tile rows),
+// then the remaining rows with a split of their own.  Only the remaining rows' partials then go
+// through the workspace and the reduce (measured on MI355X, WGRAD 12288 x 2048 x 16384: 487 us as
+// one split launch, 432 us as 8192 unsplit rows + 4096 split rows).  0 = no such part.
+static int64_t leading_rows(int64_t M, int64_t N, int64_t K) {
+  constexpr int64_t kWave = 256;                 // workgroups per wave (one per CU), as choose_splits
+  const int64_t tn = (N + kBN - 1) / kBN, tm = (M + kBM - 1) / kBM;
+  if (kWave % tn != 0) return 0;                 // a wave must be whole tile rows
+  const int64_t rows_per_wave = kWave / tn;
+  const int64_t waves = tm / rows_per_wave;
+  if (waves == 0 || waves * rows_per_wave == tm) return 0;
+  if (choose_splits(M, N, K) == 1) return 0;
+  const int64_t M1 = waves * rows_per_wave * kBM;
+  if (choose_splits(M - M1, N, K) == 1) return 0;
+  return M1;
+}
+
+hipError_t launch_gemm(int mode, int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
+                       const float* sA, const uint8_t* B, int64_t ldb, const float* sB, void* C,
+                       int64_t ldc, bool out_bf16, bool accumulate, uint8_t* q, int64_t ldq, float* qs,
+                       void* workspace, size_t workspace_bytes, hipStream_t st) {
+  if (accumulate && out_bf16) return hipErrorInvalidValue;
+  if (q != nullptr && !out_bf16) return hipErrorInvalidValue;
+  if (K == 0) {
+    if (accumulate) return hipSuccess;   // C + 0
+    if (q != nullptr) {
+      const int64_t gy = M < 65535 ? M : 65535;
+      hipLaunchKernelGGL(zero_fill_kernel, dim3(8, (unsigned)gy), dim3(256), 0, st, C, M, N * 2, ldc * 2);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      return launch_quant_1x128(C, M, N, ldc, q, ldq, qs, st);
+    }
+
+    const int64_t es = out_bf16 ? 2 : 4;
+    const int64_t gy = M < 65535 ? M : 65535;
+    hipLaunchKernelGGL(zero_fill_kernel, dim3(8, (unsigned)gy), dim3(256), 0, st, C, M, N * es, ldc * es);
+    return hipGetLastError();
+  }
+  // (the fused output quantization writes its scales with stride M: no row ranges there)
+  const int64_t M1 = q == nullptr ? leading_rows(M, N, K) : 0;
+  if (M1 > 0) {
+    const int64_t es = out_bf16 ? 2 : 4;
+    hipError_t e = launch_rows(mode, M1, N, K, A, lda, sA, M, B, ldb, sB, C, ldc, out_bf16, accumulate, nullptr, 0,
+                               nullptr, workspace, workspace_bytes, st);
+    if (e != hipSuccess) return e;
+    // sA (and the MX E8M0 tiles, 4 bytes per row) of row M1 start M1 elements in
+    return launch_rows(mode, M - M1, N, K, A + M1 * lda, lda, sA + M1, M, B, ldb, sB,
+                       static_cast<uint8_t*>(C) + M1 * ldc * es, ldc, out_bf16, accumulate, nullptr, 0, nullptr,
+                       workspace, workspace_bytes, st);
+  }
+  return launch_rows(mode, M, N, K, A, lda, sA, M, B, ldb, sB, C, ldc, out_bf16, accumulate, q, ldq, qs, workspace,
+                     workspace_bytes, st);
 }
 
 }  // namespace puro

@@ -179,6 +179,64 @@ def test_gemm_full_size_sampled(P, wname, dout, din, mode):
     assert bool(t.isfinite(C).all())
 
 
+# 8448 x 2048 tiles are 33 x 8 = 264 > one wave of 256: the library runs the first 8192 rows (one
+# whole wave of tiles) without a contraction split and splits only the last 256 rows.
+ROW_SPLIT = (8448, 2048, 16384)
+
+
+def row_split_rows(M, seed):
+    rng = np.random.default_rng(seed)
+    return np.sort(np.concatenate([rng.choice(8192, size=48, replace=False),
+                                   8192 + rng.choice(M - 8192, size=48, replace=False)]))
+
+
+def test_gemm_row_split_sampled(P):
+    """WGRAD whose leading whole wave of tiles runs unsplit and whose remaining rows are split:
+    sampled rows of both parts within the GEMM bar; the accumulating variant adds C exactly once."""
+    t = torch()
+    M, N, K = ROW_SPLIT
+    say(f"[row split gemm] WGRAD M,N,K={M},{N},{K} (unsplit rows 0..8191, split rows 8192..{M - 1})")
+    assert P.puro_fp8_gemm_workspace_size(P.WGRAD, M, N, K) > 0
+    A, sA, B, sB = gemm_case("WGRAD", M, N, K, 77)
+    C = P.puro_fp8_gemm(P.WGRAD, A, sA, B, sB, out_dtype=P.OUT_FP32)
+    C0 = t.randn((M, N), generator=gen(78), device="cuda")
+    Cacc = C0.clone()
+    P.puro_fp8_gemm_accumulate(P.WGRAD, A, sA, B, sB, Cacc)
+    t.cuda.synchronize()
+    assert bool((Cacc.view(t.int32) == (C0 + C).view(t.int32)).all()), "accumulate is not C + result"
+    rows = row_split_rows(M, 79)
+    cols = np.sort(np.random.default_rng(80).choice(N, size=64, replace=False))
+    rt, ct = t.from_numpy(rows).cuda(), t.from_numpy(cols).cuda()
+    Ad = gemm.dequant_a(host(A[rt]), host(sA[:, rt]))
+    Bd = gemm.dequant_b("WGRAD", host(B[ct]), host(sB[:, ct]))
+    ref = Ad @ Bd.T
+    err, diff, den = normalized_error(host(C[rt][:, ct]), ref, np.sqrt((Ad * Ad).sum(1)), np.sqrt((Bd * Bd).sum(1)))
+    say(f"    max normalized error {err:.3e}")
+    assert (diff <= TIGHT * den).all()
+
+
+def test_mx_gemm_row_split_sampled(P):
+    from oracle import mx
+    t = torch()
+    M, N, K = ROW_SPLIT
+    say(f"[row split mx gemm] M,N,K={M},{N},{K}")
+    A, B = e4m3_codes((M, K), 81), e4m3_codes((N, K), 82)
+    g = gen(83)
+    xa = t.randint(115, 136, (K // 128, M, 4), generator=g, device="cuda", dtype=t.uint8)
+    xb = t.randint(115, 136, (K // 128, N, 4), generator=g, device="cuda", dtype=t.uint8)
+    C = P.puro_fp8_mx_gemm(A, xa, B, xb, out_dtype=P.OUT_FP32)
+    t.cuda.synchronize()
+    rows = row_split_rows(M, 84)
+    cols = np.sort(np.random.default_rng(85).choice(N, size=64, replace=False))
+    rt, ct = t.from_numpy(rows).cuda(), t.from_numpy(cols).cuda()
+    Ad = mx.dequant(host(A[rt]), host(xa[:, rt]))
+    Bd = mx.dequant(host(B[ct]), host(xb[:, ct]))
+    ref = Ad @ Bd.T
+    err, diff, den = normalized_error(host(C[rt][:, ct]), ref, np.sqrt((Ad * Ad).sum(1)), np.sqrt((Bd * Bd).sum(1)))
+    say(f"    max normalized error {err:.3e}")
+    assert (diff <= TOL * den).all()
+
+
 # --------------------------------------------------------------------------- MXFP8 variant
 
 @pytest.mark.parametrize("wname,dout,din", WEIGHTS)
