@@ -121,23 +121,28 @@ def summarize_pmc(fetch_dir: str, write_dir: str):
             raise SystemExit(f"{counter}: the calibration copy was not found")
         factors[counter] = (COPY_BYTES, copies[0] * 1024.0)
         scale = COPY_BYTES / (copies[0] * 1024.0)
-        last = None        # a split GEMM's reduce kernel runs right after the GEMM kernel
+        # One op can be several dispatches: a split GEMM's reduce kernel runs right after the GEMM
+        # kernel, and a GEMM whose leading rows run unsplit is two launches of the same GEMM kernel
+        # in a row (no GEMM op of the bench follows another of the same kernel).
+        last, prev = None, None
         for n, v in rows:
             op = last if "split_reduce" in n else op_of_kernel(n)
+            cont = "split_reduce" in n or ("gemm_kernel" in n and n == prev)
+            prev = n
             if op is None or op == "copy":
                 continue
             if "gemm_kernel" in n:
                 last = op
             e = res.setdefault(op, {"FETCH_SIZE": 0.0, "WRITE_SIZE": 0.0, "launches": 0})
             e[counter] += v * 1024.0 * scale
-            if counter == "FETCH_SIZE" and "split_reduce" not in n:
+            if counter == "FETCH_SIZE" and not cont:
                 e["launches"] += 1
     lines = ["# HBM traffic per launch: layer sweep, 16384 tokens, seed 0 (bench step)",
              "# rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/pmc_fetch -o pmc -- python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline",
              "# rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/pmc_write -o pmc -- python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline",
              "# python bench.py --summarize-pmc OUT/pmc_fetch OUT/pmc_write   (OUT: the counter runs' output directory)",
              "# counters are scaled so that the calibration copy (256 MiB read + 256 MiB written) reads its own size;",
-             "# a GEMM op includes its split-K reduce kernel",
+             "# a GEMM op includes its split-K reduce kernel and both launches of a row-split GEMM",
              f"kernel_source_hash {kernel_source_hash()}"]
     for c, (b, measured) in factors.items():
         lines.append(f"calibration {c} copy_bytes {b} counter_bytes {measured:.0f} factor {b / measured:.4f}")
@@ -278,7 +283,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=1024)
+    ap.add_argument("--cpu-tokens", type=int, default=2048)
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     args = ap.parse_args()
     if args.summarize_pmc:
