@@ -244,6 +244,18 @@ def build_step(P, torch, d):
     return ops, single, mxops, keep
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (Linux), for the oracle timing's record."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown CPU"
+
+
 def cpu_baseline(d, tokens: int):
     """The oracle, as it stands, on the first `tokens` tokens of the same step (all 4 weights)."""
     import numpy as np
@@ -273,7 +285,7 @@ def cpu_baseline(d, tokens: int):
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"first {tokens} of 16384 tokens of the same step (all 4 weights: full 128x128 weight "
                       f"quantization, 1x128 and 128x1 activation/gradient quantization, float64 FWD/DGRAD/WGRAD); "
-                      f"{dt:.1f} s on {os.cpu_count()} host cpus",
+                      f"{dt:.1f} s on {os.cpu_count()} host cpus ({cpu_model()})",
             "seconds": dt}
 
 
@@ -370,7 +382,8 @@ def main():
         for name, e in per.items():
             tot = sum(e["ms"])
             row = {"in_step": in_step, "launches_per_step": e["launches"] // iters,
-                   "avg_us": round(1000 * tot / len(e["ms"]), 2)}
+                   "avg_us": round(1000 * tot / len(e["ms"]), 2),
+                   "median_us": round(1000 * statistics.median(e["ms"]), 2)}
             if in_step:
                 row["share_of_step"] = round(tot / total_ms, 4)
             if e["kind"] == "gemm":
