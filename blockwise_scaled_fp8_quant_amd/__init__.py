@@ -19,6 +19,7 @@ __all__ = [
     "puro_fp8_quant_w_128x128", "puro_fp8_gemm", "puro_fp8_gemm_accumulate", "puro_fp8_gemm_workspace_size",
     "puro_fp8_cast_e4m3", "puro_fp8_strerror", "puro_fp8_version", "EXPORTED_SYMBOLS",
     "puro_fp8_mx_quant_dual", "puro_fp8_mx_gemm", "puro_fp8_mx_gemm_workspace_size", "puro_fp8_gemm_quant",
+    "puro_fp8_quant_w_128x128_batch",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpuro_fp8.so")
@@ -32,6 +33,7 @@ EXPORTED_SYMBOLS = (
     "puro_fp8_gemm", "puro_fp8_gemm_accumulate", "puro_fp8_gemm_workspace_size", "puro_fp8_cast_e4m3",
     "puro_fp8_strerror", "puro_fp8_version",
     "puro_fp8_mx_quant_dual", "puro_fp8_mx_gemm", "puro_fp8_mx_gemm_workspace_size", "puro_fp8_gemm_quant",
+    "puro_fp8_quant_w_128x128_batch",
 )
 
 if not os.path.exists(LIB_PATH):
@@ -65,6 +67,15 @@ lib.puro_fp8_quant_act_1x128.argtypes = [_p, _i64, _i64, _i64, _p, _i64, _p, _p]
 lib.puro_fp8_quant_act_128x1.argtypes = [_p, _i64, _i64, _i64, _p, _i64, _p, _p]
 lib.puro_fp8_quant_act_dual.argtypes = [_p, _i64, _i64, _i64, _p, _i64, _p, _p, _i64, _p, _p]
 lib.puro_fp8_quant_w_128x128.argtypes = [_p, _i64, _i64, _i64, _p, _i64, _p, _p, _i64, _p, _p]
+
+
+class WqJob(ctypes.Structure):
+    """puro_fp8_wq_job (include/puro_fp8.h): the arguments of one 128x128 weight quantization."""
+    _fields_ = [("w", _p), ("N", _i64), ("K", _i64), ("ldw", _i64), ("q", _p), ("ldq", _i64), ("s", _p),
+                ("qT", _p), ("ldqT", _i64), ("sT", _p)]
+
+
+lib.puro_fp8_quant_w_128x128_batch.argtypes = [ctypes.POINTER(WqJob), _int, _p]
 lib.puro_fp8_gemm.argtypes = [_int, _i64, _i64, _i64, _p, _i64, _p, _p, _i64, _p, _p, _i64, _int, _p, _sz, _p]
 lib.puro_fp8_gemm_accumulate.argtypes = [_int, _i64, _i64, _i64, _p, _i64, _p, _p, _i64, _p, _p, _i64, _p, _sz, _p]
 lib.puro_fp8_gemm_quant.argtypes = [_int, _i64, _i64, _i64, _p, _i64, _p, _p, _i64, _p, _p, _i64, _p, _i64, _p, _p, _sz, _p]
@@ -182,6 +193,32 @@ def puro_fp8_quant_w_128x128(w, q=None, s=None, qT=None, sT=None, transposed: bo
     _check(lib.puro_fp8_quant_w_128x128(_ptr(w), N, K, _ld(w), _ptr(q), _ld(q), _ptr(s), _ptr(qT), ldqT,
                                         _ptr(sT), _stream(stream)), "puro_fp8_quant_w_128x128")
     return q, s, qT, sT
+
+
+def puro_fp8_quant_w_128x128_batch(weights, outs=None, transposed: bool = True, stream=None):
+    """Several weights in one launch: weights = [w bf16 [N, K], ...]; outs (optional) = [(q, s, qT, sT),
+    ...] as puro_fp8_quant_w_128x128 takes them.  Returns [(q, s, qT, sT), ...], the same bytes as one
+    puro_fp8_quant_w_128x128 call per weight."""
+    torch = _torch()
+    res = []
+    jobs = (WqJob * max(len(weights), 1))()
+    for i, w in enumerate(weights):
+        N, K = w.shape
+        q, s, qT, sT = outs[i] if outs is not None else (None, None, None, None)
+        if q is None:
+            q = torch.empty((N, K), dtype=torch.uint8, device=w.device)
+        if s is None:
+            s = torch.empty((N // 128, K // 128), dtype=torch.float32, device=w.device)
+        if transposed:
+            if qT is None:
+                qT = torch.empty((K, N), dtype=torch.uint8, device=w.device)
+            if sT is None:
+                sT = torch.empty((K // 128, N // 128), dtype=torch.float32, device=w.device)
+        jobs[i] = WqJob(_ptr(w), N, K, _ld(w), _ptr(q), _ld(q), _ptr(s), _ptr(qT),
+                        _ld(qT) if qT is not None else 0, _ptr(sT))
+        res.append((q, s, qT, sT))
+    _check(lib.puro_fp8_quant_w_128x128_batch(jobs, len(weights), _stream(stream)), "puro_fp8_quant_w_128x128_batch")
+    return res
 
 
 def puro_fp8_gemm_workspace_size(mode: int, M: int, N: int, K: int) -> int:

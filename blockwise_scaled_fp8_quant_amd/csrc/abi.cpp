@@ -63,8 +63,9 @@ int puro_fp8_quant_act_dual(const void* x, int64_t T, int64_t C, int64_t ldx, ui
   return from_hip(puro::launch_quant_dual(x, T, C, ldx, q, ldq, s, qT, ldqT, sT, st));
 }
 
-int puro_fp8_quant_w_128x128(const void* w, int64_t N, int64_t K, int64_t ldw, uint8_t* q, int64_t ldq,
-                             float* s, uint8_t* qT, int64_t ldqT, float* sT, hipStream_t st) {
+// Argument checks of one 128x128 weight quantization (PURO_OK also for an empty weight).
+static int check_quant_w(const void* w, int64_t N, int64_t K, int64_t ldw, const uint8_t* q, int64_t ldq,
+                         const float* s, const uint8_t* qT, int64_t ldqT, const float* sT) {
   if (N < 0 || K < 0) return PURO_ERR_SHAPE;
   if (N % kGroup || K % kGroup) return PURO_ERR_SHAPE;
   if ((qT == nullptr) != (sT == nullptr)) return PURO_ERR_NULLPTR;
@@ -75,7 +76,32 @@ int puro_fp8_quant_w_128x128(const void* w, int64_t N, int64_t K, int64_t ldw, u
   if (ldw < K || ldq < K || (ldw * 2) % 16 || ldq % 16) return PURO_ERR_LD;
   if (qT && (ldqT < N || ldqT % 16)) return PURO_ERR_LD;
   if (too_many_blocks(N / kGroup, K / kGroup)) return PURO_ERR_UNSUPPORTED;
+  return PURO_OK;
+}
+
+int puro_fp8_quant_w_128x128(const void* w, int64_t N, int64_t K, int64_t ldw, uint8_t* q, int64_t ldq,
+                             float* s, uint8_t* qT, int64_t ldqT, float* sT, hipStream_t st) {
+  const int rc = check_quant_w(w, N, K, ldw, q, ldq, s, qT, ldqT, sT);
+  if (rc != PURO_OK || N == 0 || K == 0) return rc;
   return from_hip(puro::launch_quant_128x128(w, N, K, ldw, q, ldq, s, qT, ldqT, sT, st));
+}
+
+int puro_fp8_quant_w_128x128_batch(const puro_fp8_wq_job* jobs, int n_jobs, hipStream_t st) {
+  if (n_jobs < 0 || n_jobs > puro::kMaxWeightJobs) return PURO_ERR_UNSUPPORTED;
+  if (n_jobs == 0) return PURO_OK;
+  if (!jobs) return PURO_ERR_NULLPTR;
+  puro::WeightJob b[puro::kMaxWeightJobs];
+  int64_t blocks = 0;
+  for (int i = 0; i < n_jobs; ++i) {
+    const puro_fp8_wq_job& j = jobs[i];
+    const int rc = check_quant_w(j.w, j.N, j.K, j.ldw, j.q, j.ldq, j.s, j.qT, j.ldqT, j.sT);
+    if (rc != PURO_OK) return rc;
+    b[i] = puro::WeightJob{static_cast<const uint16_t*>(j.w), j.N, j.K, j.ldw, j.q, j.ldq, j.s, j.qT, j.ldqT, j.sT,
+                           0, 0};
+    blocks += (j.N / kGroup) * (j.K / kGroup);
+  }
+  if (blocks > 0x7FFFFFFF) return PURO_ERR_UNSUPPORTED;
+  return from_hip(puro::launch_quant_128x128_batch(b, n_jobs, st));
 }
 
 static int gemm_common(int mode, int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda, const float* sA,

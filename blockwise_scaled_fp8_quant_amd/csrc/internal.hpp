@@ -21,6 +21,27 @@ hipError_t launch_quant_128x128(const void* w, int64_t N, int64_t K, int64_t ldw
                                 hipStream_t st);
 hipError_t launch_cast_e4m3(const float* v, int64_t n, uint8_t* q, hipStream_t st);
 
+// Several 128x128 weight quantizations in one launch (each exactly as launch_quant_128x128).
+// bt and first are filled in by the launcher.
+struct WeightJob {
+  const uint16_t* w;
+  int64_t N, K, ldw;
+  uint8_t* q;
+  int64_t ldq;
+  float* s;
+  uint8_t* qT;     // optional (with sT)
+  int64_t ldqT;
+  float* sT;
+  int bt;          // token-run length of the job's tile order
+  int64_t first;   // the job's first block in the launch
+};
+constexpr int kMaxWeightJobs = 16;
+struct WeightJobs {
+  WeightJob job[kMaxWeightJobs];
+  int n;
+};
+hipError_t launch_quant_128x128_batch(const WeightJob* jobs, int n, hipStream_t st);
+
 // GEMM: mode 0 FWD, 1 DGRAD, 2 WGRAD, 3 MXFP8 (E8M0 block scales, bytes [K/128][rows][4]); out_bf16 selects bf16 (else fp32) output; accumulate
 // (fp32 output only) adds the result to C; q / ldq / qs (bf16 output only, optional) also
 // write the 1x128 quantization of the bf16 C along N (codes [M, N], scales [N/128][M]).

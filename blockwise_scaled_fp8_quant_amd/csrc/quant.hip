@@ -429,12 +429,11 @@ __global__ __launch_bounds__(256) void mx_quant_dual_kernel(const uint16_t* __re
 // of consecutive N blocks of one K block (tile_order), so each qT row is written in long
 // contiguous runs.
 // ---------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void quant_128x128_kernel(const uint16_t* __restrict__ w, int64_t N,
-                                                            int64_t K, int64_t ldw,
-                                                            uint8_t* __restrict__ q, int64_t ldq,
-                                                            float* __restrict__ s,
-                                                            uint8_t* __restrict__ qT, int64_t ldqT,
-                                                            float* __restrict__ sT, int bt) {
+// One 128 x 128 block (number blk of the weight's tile order) of one weight.
+__device__ __forceinline__ void quant_128x128_block(const uint16_t* __restrict__ w, int64_t N, int64_t K, int64_t ldw,
+                                                    uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ s,
+                                                    uint8_t* __restrict__ qT, int64_t ldqT, float* __restrict__ sT,
+                                                    int bt, int64_t blk) {
   __shared__ uint32_t red[4];
   __shared__ uint32_t stage[128 * 33];
   const int t = threadIdx.x;
@@ -443,7 +442,7 @@ __global__ __launch_bounds__(256) void quant_128x128_kernel(const uint16_t* __re
   const int cc = t & 15;
   const int rg = t >> 4;
   int64_t nb, kb;
-  tile_order(blockIdx.x, K >> 7, bt, nb, kb);
+  tile_order(blk, K >> 7, bt, nb, kb);
   const int64_t n0 = nb * 128 + rg * 8;
   const int64_t k0 = kb * 128 + cc * 8;
 
@@ -501,6 +500,25 @@ __global__ __launch_bounds__(256) void quant_128x128_kernel(const uint16_t* __re
       __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(qT + (kb * 128 + cl) * ldqT + nb * 128 + part * 16));
     }
   }
+}
+
+__global__ __launch_bounds__(256) void quant_128x128_kernel(const uint16_t* __restrict__ w, int64_t N,
+                                                            int64_t K, int64_t ldw,
+                                                            uint8_t* __restrict__ q, int64_t ldq,
+                                                            float* __restrict__ s,
+                                                            uint8_t* __restrict__ qT, int64_t ldqT,
+                                                            float* __restrict__ sT, int bt) {
+  quant_128x128_block(w, N, K, ldw, q, ldq, s, qT, ldqT, sT, bt, blockIdx.x);
+}
+
+// Several weights in one launch: job j owns blocks first[j] .. first[j + 1) - 1 (a wave-uniform
+// scan over at most kMaxWeightJobs jobs), each in its own tile order.
+__global__ __launch_bounds__(256) void quant_128x128_batch_kernel(WeightJobs jobs) {
+  int j = jobs.n - 1;
+  while (j > 0 && (int64_t)blockIdx.x < jobs.job[j].first) --j;
+  const WeightJob& b = jobs.job[j];
+  quant_128x128_block(b.w, b.N, b.K, b.ldw, b.q, b.ldq, b.s, b.qT, b.ldqT, b.sT, b.bt,
+                      (int64_t)blockIdx.x - b.first);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -561,6 +579,27 @@ hipError_t launch_mx_quant_dual(const void* x, int64_t T, int64_t C, int64_t ldx
   if (nb * ng > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(mx_quant_dual_kernel, dim3((unsigned)(nb * ng)), dim3(256), 0, st,
                      static_cast<const uint16_t*>(x), T, C, ldx, q, ldq, xs, qT, ldqT, xsT, token_run(nb));
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_128x128_batch(const WeightJob* jobs, int n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  if (n > kMaxWeightJobs) return hipErrorInvalidValue;
+  WeightJobs a;
+  int64_t total = 0;
+  a.n = 0;
+  for (int i = 0; i < n; ++i) {
+    const int64_t blocks = (jobs[i].N / 128) * (jobs[i].K / 128);
+    if (blocks == 0) continue;                   // empty weights take no blocks
+    a.job[a.n] = jobs[i];
+    a.job[a.n].bt = token_run(jobs[i].N / 128);
+    a.job[a.n].first = total;
+    total += blocks;
+    ++a.n;
+  }
+  if (a.n == 0) return hipSuccess;
+  if (total > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(quant_128x128_batch_kernel, dim3((unsigned)total), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -118,6 +118,35 @@ int puro_fp8_quant_w_128x128(const void* w, int64_t N, int64_t K, int64_t ldw,
                              uint8_t* qT, int64_t ldqT, float* sT, hipStream_t st);
 
 /*
+ * One weight of puro_fp8_quant_w_128x128_batch: the arguments of puro_fp8_quant_w_128x128, with
+ * the same meaning, layouts and rules.
+ */
+typedef struct puro_fp8_wq_job {
+  const void* w;
+  int64_t N, K, ldw;
+  uint8_t* q;
+  int64_t ldq;
+  float* s;
+  uint8_t* qT;   /* optional, with sT */
+  int64_t ldqT;
+  float* sT;
+} puro_fp8_wq_job;
+
+/*
+ * Several 128x128 weight quantizations in one launch.  Every job writes exactly the bytes that
+ * puro_fp8_quant_w_128x128 with its arguments writes.  The weights of a layer do not depend on
+ * the activations, and the pages train with BF16/FP32 master weights (agihunt digest, section
+ * 方法, FP8 bullet), so all of a layer's weights are quantized anew after each optimizer step:
+ * one launch then replaces one small launch per weight.
+ *   jobs   : host array of n_jobs descriptors (read before the call returns; not kept).
+ *   n_jobs : 0 .. 16 (else PURO_ERR_UNSUPPORTED); 0 does nothing.
+ * Every job is checked as puro_fp8_quant_w_128x128 checks its arguments before anything is
+ * launched; the first failing job's error is returned and nothing runs.  Jobs must not write
+ * overlapping outputs.
+ */
+int puro_fp8_quant_w_128x128_batch(const puro_fp8_wq_job* jobs, int n_jobs, hipStream_t st);
+
+/*
  * Blockwise-scaled FP8 GEMM  C[M,N] = sum_kb sA(i,kb) sB(j,kb) sum_{k in kb} dec(A[i,k]) dec(B[j,k]).
  * ModelScope write-up, section 精度 (FP8 matmuls of the main linear layers, DeepSeek-V3
  * block scaling); per-slice fp32 promotion into a separate fp32 accumulator.

@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_header_and_binding_agree():
     decl = declared_functions()
-    assert len(decl) == 14
+    assert len(decl) == 15
     assert sorted(P.EXPORTED_SYMBOLS) == decl
 
 
@@ -97,6 +97,31 @@ def test_quant_w_validation():
     assert qw(qT=None) == NULLPTR and qw(sT=None) == NULLPTR and qw(w=None) == NULLPTR
     assert qw(qT=MIS) == ALIGN and qw(w=MIS) == ALIGN
     assert qw(ldw=128) == LD and qw(ldqT=128) == LD and qw(ldq=264) == LD
+
+
+def wjob(w=A16, N=256, K=256, ldw=256, q=A16, ldq=256, s=A16, qT=A16, ldqT=256, sT=A16):
+    return P.WqJob(w, N, K, ldw, q, ldq, s, qT, ldqT, sT)
+
+
+def qwb(*jobs, n=None):
+    arr = (P.WqJob * max(len(jobs), 1))(*jobs)
+    return P.lib.puro_fp8_quant_w_128x128_batch(arr, len(jobs) if n is None else n, None)
+
+
+def test_quant_w_batch_validation():
+    # every job is checked as the single-weight call checks it, before anything is launched: each
+    # batch below holds at least one failing job (so no kernel runs here)
+    assert P.lib.puro_fp8_quant_w_128x128_batch(None, 0, None) == OK
+    assert P.lib.puro_fp8_quant_w_128x128_batch(None, 2, None) == NULLPTR
+    assert qwb(wjob(), n=17) == UNSUP and qwb(wjob(), n=-1) == UNSUP
+    assert qwb(wjob(N=200)) == SHAPE
+    assert qwb(wjob(), wjob(K=64)) == SHAPE                       # the second job fails
+    assert qwb(wjob(), wjob(), wjob(qT=None)) == NULLPTR
+    assert qwb(wjob(N=0), wjob(w=MIS)) == ALIGN                   # an empty job is skipped, not accepted blindly
+    assert qwb(wjob(), wjob(ldw=128)) == LD and qwb(wjob(ldq=264), wjob()) == LD
+    # the same errors as one call per weight
+    for bad in (dict(N=200), dict(qT=None), dict(w=MIS), dict(ldqT=128)):
+        assert qwb(wjob(**bad)) == qw(**bad)
 
 
 def gm(mode=0, M=256, N=256, K=256, A=A16, lda=256, sA=A16, B=A16, ldb=256, sB=A16, C=A16, ldc=256,
