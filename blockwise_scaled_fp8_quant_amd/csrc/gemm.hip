@@ -33,6 +33,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include "codec.hpp"
 #include "internal.hpp"
@@ -492,17 +493,18 @@ template <int MODE, bool BF16, bool QUANT = false>
 static hipError_t launch_one(const GemmArgs& a, hipStream_t st) {
   const int smem = 2 * kStageBytes;
   // The dynamic-LDS limit is a per-device attribute of the kernel: set it once per device the
-  // caller launches on (benign race: every caller sets the same value).
+  // caller launches on (threads that race here all set the same value).
   constexpr int kMaxDevices = 64;
-  static bool attr_set[kMaxDevices] = {};
+  static std::atomic<bool> attr_set[kMaxDevices];
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= kMaxDevices || !attr_set[dev]) {
+  const bool known = dev >= 0 && dev < kMaxDevices;
+  if (!known || !attr_set[dev].load(std::memory_order_acquire)) {
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<MODE, BF16, QUANT>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, smem);
     if (e != hipSuccess) return e;
-    if (dev >= 0 && dev < kMaxDevices) attr_set[dev] = true;
+    if (known) attr_set[dev].store(true, std::memory_order_release);
   }
   hipLaunchKernelGGL((gemm_kernel<MODE, BF16, QUANT>), dim3(a.tiles_m * a.tiles_n * a.splits), dim3(kThreads), smem, st, a);
   return hipGetLastError();
