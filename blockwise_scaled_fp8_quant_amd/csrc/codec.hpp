@@ -1,4 +1,5 @@
-// Device-side E4M3 codec and tile-scale helpers shared by the gfx950 quantizer kernels.
+// Device-side E4M3 codec and tile-scale helpers shared by the gfx950 quantizer kernels and
+// the GEMM epilogue's fused 1x128 output quantization.
 //
 // Tile numerics (the pages fix only "FP8, activations per 128, weights per 128x128
 // block, one scale per block"; the readings below are this library's):

@@ -24,10 +24,12 @@
 //    (FWD/DGRAD) the whole scale product is one multiply per lane and slice, and the
 //    promotion is one FMA per accumulator element per slice.
 //  * Tiles are visited in an XCD-aware order: the dispatcher places workgroup b on XCD
-//    b % 8, so each XCD is given a contiguous run of tiles, walked in groups of 8 tile
-//    rows, so that the tiles resident in one XCD's L2 share A rows and B columns.
+//    b % 8, so each XCD is given a contiguous run of tiles, walked in groups of 4 or 8 tile
+//    rows (choose_group), so that the tiles resident in one XCD's L2 share A rows and B
+//    columns.
 //  * The epilogue stages each wave's output tile in LDS and writes whole row segments
-//    with 16-byte stores (a lane's own fragment holds 4 columns of 16 rows).
+//    with 16-byte stores (a lane's own fragment holds one row of a 32x32 tile, as 4 runs
+//    of 4 adjacent columns).
 //  * M or N that are multiples of 128 but not of 256 leave half-empty edge tiles: their
 //    loads are clamped to valid rows and their stores are masked.
 #include <hip/hip_runtime.h>

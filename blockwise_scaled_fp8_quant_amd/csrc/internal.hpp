@@ -42,9 +42,10 @@ struct WeightJobs {
 };
 hipError_t launch_quant_128x128_batch(const WeightJob* jobs, int n, hipStream_t st);
 
-// GEMM: mode 0 FWD, 1 DGRAD, 2 WGRAD, 3 MXFP8 (E8M0 block scales, bytes [K/128][rows][4]); out_bf16 selects bf16 (else fp32) output; accumulate
-// (fp32 output only) adds the result to C; q / ldq / qs (bf16 output only, optional) also
-// write the 1x128 quantization of the bf16 C along N (codes [M, N], scales [N/128][M]).
+// GEMM: mode 0 FWD, 1 DGRAD, 2 WGRAD, 3 MXFP8 (E8M0 block scales, bytes [K/128][rows][4]);
+// out_bf16 selects bf16 (else fp32) output; accumulate (fp32 output only) adds the result to
+// C; q / ldq / qs (bf16 output only, optional) also write the 1x128 quantization of the bf16
+// C along N (codes [M, N], scales [N/128][M]).
 size_t gemm_workspace_bytes(int mode, int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm(int mode, int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
                        const float* sA, const uint8_t* B, int64_t ldb, const float* sB, void* C,

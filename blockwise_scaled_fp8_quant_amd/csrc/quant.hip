@@ -1,12 +1,14 @@
 // gfx950 quantizer kernels: 1x128 activation groups, 128x1 token groups written
-// transposed (wgrad operands), 128x128 weight blocks (+ optional transposed copy), and
-// the standalone fp32 -> E4M3 cast used to verify the device codec.
+// transposed (wgrad operands), 128x128 weight blocks (+ optional transposed copy, one
+// weight or a batch of them per launch), the dual quantizer (1x128 and transposed 128x1
+// codes from one read), its MXFP8 counterpart (32-element blocks, E8M0 scales), and the
+// standalone fp32 -> E4M3 cast used to verify the device codec.
 //
-// All three quantizers are HBM-bound streams (2 B read + 1 B written per element plus
-// one 4-byte scale per tile); the kernels use 16-byte coalesced loads and stores, keep
-// the tile in registers, reduce amax with DPP / cross-lane moves (and LDS across waves
-// where a tile spans waves), and run the per-element work as one fp32 multiply and half
-// a packed FP8 convert.
+// All of them are HBM-bound streams (2 B read + 1 B written per element and orientation,
+// plus one scale per tile); the kernels use 16-byte coalesced loads and stores, keep the
+// tile in registers, reduce amax with DPP / cross-lane moves (and LDS across waves where a
+// tile spans waves), and run the per-element work as one fp32 multiply and half a packed
+// FP8 convert.
 #include "codec.hpp"
 #include "internal.hpp"
 
