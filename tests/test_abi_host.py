@@ -245,3 +245,32 @@ def test_product_path_never_imports_oracle():
             if f.endswith((".py", ".hip", ".cpp", ".hpp", ".h")):
                 src = open(os.path.join(dirpath, f)).read()
                 assert "from oracle" not in src and "import oracle" not in src, f
+
+
+def test_binding_rejects_host_tensors_before_any_call():
+    """The binding checks what the C ABI cannot see (device, dtype, shape, layout) and raises before
+    passing a pointer on: a host tensor never reaches the library."""
+    import torch
+    x = torch.zeros((128, 128), dtype=torch.bfloat16)
+    q = torch.zeros((128, 128), dtype=torch.uint8)
+    s = torch.zeros((1, 128), dtype=torch.float32)
+    with pytest.raises(ValueError, match="must be a GPU tensor"):
+        P.puro_fp8_quant_act_1x128(x)
+    with pytest.raises(ValueError, match="must be a GPU tensor"):
+        P.puro_fp8_quant_act_dual(x)
+    with pytest.raises(ValueError, match="must be a GPU tensor"):
+        P.puro_fp8_quant_w_128x128(x)
+    with pytest.raises(ValueError, match="must be a GPU tensor"):
+        P.puro_fp8_quant_w_128x128_batch([x])
+    with pytest.raises(ValueError, match="must be a GPU tensor"):
+        P.puro_fp8_gemm(P.FWD, q, s, q, torch.zeros((1, 1)))
+    with pytest.raises(ValueError, match="must be a GPU tensor"):
+        P.puro_fp8_mx_gemm(q, torch.zeros((1, 128, 4), dtype=torch.uint8), q, torch.zeros((1, 128, 4), dtype=torch.uint8))
+    with pytest.raises(ValueError, match="must be a GPU tensor"):
+        P.puro_fp8_cast_e4m3(torch.zeros(16))
+    with pytest.raises(ValueError, match="2-D"):
+        P.puro_fp8_quant_act_1x128(torch.zeros(128, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="contraction length"):
+        P.puro_fp8_gemm(P.FWD, q, s, torch.zeros((128, 256), dtype=torch.uint8), torch.zeros((1, 2)))
+    with pytest.raises(ValueError, match="out_dtype"):
+        P.puro_fp8_gemm(P.FWD, q, s, q, torch.zeros((1, 1)), out_dtype=7)
