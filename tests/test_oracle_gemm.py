@@ -5,7 +5,8 @@
 - the slice-wise promotion form sum_kb P_kb * sA * sB (exact per-slice partials)
   equals dequantize-then-matmul;
 - special cases: unit scales reduce to a plain FP8 matmul; one nonzero code per
-  row gives one scaled product; scaled small integers give an exact integer result.
+  row gives one scaled product; scaled small integers give an exact integer result;
+- the bf16 rounding helper against PyTorch's own float32 -> bfloat16 conversion.
 """
 import numpy as np
 import pytest
@@ -126,3 +127,20 @@ def test_sampled_rows_match_full():
         r = RNG.integers(256, size=50)
         c = RNG.integers(256, size=50)
         np.testing.assert_allclose(gemm.gemm_rows(mode, A, sA, B, sB, r, c), C[r, c], rtol=1e-13)
+
+
+def test_bf16_round_matches_torch_rne():
+    """bf16_round (used for the bit-exact bf16-output GEMM checks) against PyTorch's own
+    float32 -> bfloat16 conversion (round to nearest even): random magnitudes over a wide
+    range, every exact tie (low 16 bits 0x8000, both parities of the kept mantissa), and the
+    integers the exact-integer GEMM tests produce."""
+    import torch
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal(200000) * np.exp2(rng.integers(-100, 100, 200000).astype(np.float64))
+    hi = rng.integers(0, 1 << 16, 50000, dtype=np.uint32) & np.uint32(0x7F7F)   # finite exponents
+    ties = ((hi << np.uint32(16)) | np.uint32(0x8000)).view(np.float32).astype(np.float64)
+    ints = np.arange(-(1 << 15), 1 << 15, dtype=np.float64)
+    for v in (x, ties, -ties, ints):
+        ref = torch.from_numpy(v.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+        got = gemm.bf16_round(v)
+        assert (got == ref).all()
