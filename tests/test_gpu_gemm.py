@@ -269,3 +269,18 @@ def test_workloads_sampled(P, name, idx):
     d = draw(name)
     A, sA, B, sB = quantized_operands(mode, d[an], d[bn])
     sampled_check(P, mode, A, sA, B, sB, 0 if odt == "bf16" else 1, f"{name}[{idx}]")
+
+
+@pytest.mark.parametrize("case", range(24))
+def test_random_problem_sweep(P, case):
+    """Seeded random problems: the mode, M and N (multiples of 128, so half-empty edge tiles
+    occur), K (short contractions and ones long enough to be split), the output type and
+    padded leading dimensions of A and C are all drawn."""
+    rng = np.random.default_rng(9000 + case)
+    mode = list(MODES)[int(rng.integers(3))]
+    M, N = (128 * int(v) for v in rng.integers(1, 9, size=2))
+    K = 128 * int(rng.integers(1, 25))
+    out_dtype = int(rng.integers(2))
+    pads = {"lda_pad": 16 * int(rng.integers(0, 3)), "ldc_pad": 8 * int(rng.integers(0, 3))}
+    A, sA, B, sB = rand_case(mode, M, N, K, seed=100 + case)
+    check(P, mode, A, sA, B, sB, out_dtype, f"sweep {case}", bf16_allowance=True, **pads)

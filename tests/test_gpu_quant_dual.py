@@ -125,3 +125,17 @@ def test_dual_matches_single_quantizers(P):
     qT1, sT1 = P.puro_fp8_quant_act_128x1(x)
     for a, b, what in ((q, q1, "q"), (s, s1, "s"), (qT, qT1, "qT"), (sT, sT1, "sT")):
         assert_bytes_equal(host(a), host(b), what)
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_dual_random_shape_sweep(P, case):
+    """Seeded random shapes (token and column counts in multiples of 128, odd block counts
+    included), scales spread over many binades across rows and columns, and padded leading
+    dimensions of x, q and qT: all four outputs byte-identical to the oracle."""
+    rng = np.random.default_rng(7000 + case)
+    T = 128 * int(rng.integers(1, 12))
+    C = 128 * int(rng.integers(1, 12))
+    x = rng.standard_t(3, size=(T, C)) * np.exp2(rng.integers(-20, 20, size=(T, 1)) + rng.integers(-8, 8, size=(1, C)))
+    pads = {"ldx_pad": 8 * int(rng.integers(0, 3)), "ldq_pad": 16 * int(rng.integers(0, 3)),
+            "ldqT_pad": 16 * int(rng.integers(0, 3))}
+    check_dual(P, bf16(x), f"sweep {case}", **pads)
