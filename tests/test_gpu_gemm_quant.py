@@ -30,7 +30,10 @@ def bits(x):
 def operands(mode, M, N, K, seed):
     rng = np.random.default_rng(seed)
     A, sA = quant.quant_act_1x128(bits(rng.standard_t(3, (M, K))))
-    B, sB, BT, sBT = quant.quant_w_128x128(bits(rng.standard_normal((N, K)) * 0.02))
+    if mode == "WGRAD":      # per-row B scales [K/128, N]: the layout of a 1x128 quantization
+        B, sB = quant.quant_act_1x128(bits(rng.standard_t(3, (N, K))))
+    else:
+        B, sB, BT, sBT = quant.quant_w_128x128(bits(rng.standard_normal((N, K)) * 0.02))
     return A, sA, B, sB
 
 
@@ -68,7 +71,8 @@ def fused_vs_unfused(P, mode, M, N, K, seed, ldc_pad=0, ldq_pad=0, check_oracle=
 
 
 @pytest.mark.parametrize("mode,M,N,K", [("FWD", 256, 384, 512), ("FWD", 384, 256, 2048), ("DGRAD", 512, 640, 1024),
-                                        ("FWD", 256, 256, 16384), ("DGRAD", 128, 128, 4096)])
+                                        ("FWD", 256, 256, 16384), ("DGRAD", 128, 128, 4096),
+                                        ("WGRAD", 256, 384, 1024), ("WGRAD", 256, 256, 8192)])
 def test_gemm_quant_matches_unfused(P, mode, M, N, K):
     fused_vs_unfused(P, mode, M, N, K, M + N + K)
 
