@@ -25,6 +25,10 @@ Pins (checked by the ``-m "not gpu"`` tests, against things other than this code
                       cases (unit scales -> plain FP8 matmul; one nonzero code per
                       row -> one scaled product; scaled small integers -> exact
                       integer result).
+  gemm.operand_norms  the parity bar's denominators: an exact rational per-element
+  mx.operand_norms    loop reading each scale from the documented layout; closed
+                      forms (unit codes with power-of-two scales; one nonzero code per
+                      row); planted layout / decoding mistakes must fail these pins.
   mx.*                MXFP8 (OCP MX v1.0, E4M3 elements, blocks of 32): E8M0 decode
                       against PyTorch's float8_e8m0fnu for all 256 codes; the shared
                       exponent against a brute-force power-of-two search for every
