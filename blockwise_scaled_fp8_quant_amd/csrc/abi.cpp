@@ -11,6 +11,9 @@ namespace {
 constexpr int64_t kGroup = 128;
 constexpr int64_t kIntMax = 0x7FFFFFFF;
 constexpr int kModeMx = 3;   // the MXFP8 GEMM's internal mode (not a public PURO_GEMM_* value)
+// Largest operand row stride (bytes) of the GEMM: the kernels form each lane's copy offset inside
+// an 8-row group, 7 * ld + 127, in 32 bits.
+constexpr int64_t kMaxGemmLd = int64_t(1) << 29;
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -129,6 +132,7 @@ static int gemm_common(int mode, int64_t M, int64_t N, int64_t K, const uint8_t*
     if (lda < K || ldb < K || lda % 16 || ldb % 16) return PURO_ERR_LD;
   }
   if (M > kIntMax || N > kIntMax || K > kIntMax) return PURO_ERR_UNSUPPORTED;
+  if (K > 0 && (lda > kMaxGemmLd || ldb > kMaxGemmLd)) return PURO_ERR_UNSUPPORTED;
   const size_t need = puro::gemm_workspace_bytes(mode, M, N, K);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return PURO_ERR_WORKSPACE;
   return from_hip(puro::launch_gemm(mode, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, out_dtype == PURO_OUT_BF16,
@@ -177,6 +181,7 @@ int puro_fp8_mx_quant_dual(const void* x, int64_t T, int64_t C, int64_t ldx, uin
 int puro_fp8_gemm_accumulate(int mode, int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
                              const float* sA, const uint8_t* B, int64_t ldb, const float* sB, float* C, int64_t ldc,
                              void* workspace, size_t workspace_bytes, hipStream_t st) {
+  if (mode == kModeMx) return PURO_ERR_MODE;   // internal mode: no accumulating MX entry point
   return gemm_common(mode, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, PURO_OUT_FP32, true, workspace,
                      workspace_bytes, st);
 }

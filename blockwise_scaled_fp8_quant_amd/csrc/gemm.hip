@@ -111,7 +111,8 @@ struct GemmArgs {
   int accumulate;        // fp32 output only: C = C + result (one fp32 add per element)
   uint8_t* q;            // bf16 output only, optional: 1x128 quantization of C along N
   int64_t ldq;
-  float* qs;             // its scales [N/128][M]
+  float* qs;             // its scales: qs[nb * ldqs + i] for row i, column block nb
+  int64_t ldqs;
 };
 
 // Map the linear workgroup id to a (tile_m, tile_n) pair: XCD-contiguous, grouped rows.  The
@@ -396,7 +397,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
               cvt4(bf16_lo(o[0]) * r, bf16_hi(o[0]) * r, bf16_lo(o[1]) * r, bf16_hi(o[1]) * r);
         }
       if (h == 0 && rows_ok && cols_ok)
-        p.qs[(int64_t)((n0 >> 7) + wn) * p.M + m0 + wm * 64 + mi * 32 + l32] = sc;
+        p.qs[(int64_t)((n0 >> 7) + wn) * p.ldqs + m0 + wm * 64 + mi * 32 + l32] = sc;
     }
     __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_wave_barrier();
@@ -485,12 +486,6 @@ static int choose_splits(int64_t M, int64_t N, int64_t K) {
   return best;
 }
 
-size_t gemm_workspace_bytes(int, int64_t M, int64_t N, int64_t K) {
-  if (M <= 0 || N <= 0 || K <= 0) return 0;
-  const int sp = choose_splits(M, N, K);
-  return sp > 1 ? (size_t)sp * (size_t)M * (size_t)N * 4 : 0;
-}
-
 template <int MODE, bool BF16, bool QUANT = false>
 static hipError_t launch_one(const GemmArgs& a, hipStream_t st) {
   const int smem = 2 * kStageBytes;
@@ -524,10 +519,11 @@ static int choose_group(int64_t M, int64_t N, int64_t K) {
 
 // One GEMM launch (and its split-K reduce) over M rows of A and C; the slices of sA are ldsa
 // apart (ldsa >= M).
-static hipError_t launch_rows(int mode, int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
-                              const float* sA, int64_t ldsa, const uint8_t* B, int64_t ldb, const float* sB,
-                              void* C, int64_t ldc, bool out_bf16, bool accumulate, uint8_t* q, int64_t ldq,
-                              float* qs, void* workspace, size_t workspace_bytes, hipStream_t st) {
+static hipError_t launch_rows(int mode, int64_t M, int64_t N, int64_t K, int splits, const uint8_t* A,
+                              int64_t lda, const float* sA, int64_t ldsa, const uint8_t* B, int64_t ldb,
+                              const float* sB, void* C, int64_t ldc, bool out_bf16, bool accumulate, uint8_t* q,
+                              int64_t ldq, float* qs, int64_t ldqs, void* workspace, size_t workspace_bytes,
+                              hipStream_t st) {
   GemmArgs a;
   a.M = (int)M; a.N = (int)N; a.K = (int)K;
   a.tiles_m = (int)((M + kBM - 1) / kBM);
@@ -535,8 +531,8 @@ static hipError_t launch_rows(int mode, int64_t M, int64_t N, int64_t K, const u
   if ((int64_t)a.tiles_m * a.tiles_n > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   a.A = A; a.lda = lda; a.sA = sA; a.ldsa = ldsa; a.B = B; a.ldb = ldb; a.sB = sB; a.C = C; a.ldc = ldc;
   a.accumulate = 0;
-  a.q = nullptr; a.ldq = 0; a.qs = nullptr;
-  a.splits = choose_splits(M, N, K);
+  a.q = nullptr; a.ldq = 0; a.qs = nullptr; a.ldqs = 0;
+  a.splits = splits;
   a.group = choose_group(M, N, K);
   a.kb_per_split = (int)((K / kBK + a.splits - 1) / a.splits);
   a.split_stride = 0;
@@ -562,7 +558,7 @@ static hipError_t launch_rows(int mode, int64_t M, int64_t N, int64_t K, const u
       if (q != nullptr) {   // quantize the reduced bf16 output: the same bytes as the fused epilogue
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        return launch_quant_1x128(C, M, N, ldc, q, ldq, qs, st);
+        return launch_quant_1x128(C, M, N, ldc, q, ldq, qs, st, ldqs);
       }
     }
     else
@@ -572,7 +568,7 @@ static hipError_t launch_rows(int mode, int64_t M, int64_t N, int64_t K, const u
     return hipGetLastError();
   }
   a.accumulate = accumulate ? 1 : 0;
-  a.q = q; a.ldq = ldq; a.qs = qs;
+  a.q = q; a.ldq = ldq; a.qs = qs; a.ldqs = ldqs;
   if (q != nullptr) {
     switch (mode) {
       case 0: return launch_one<0, true, true>(a, st);
@@ -611,6 +607,32 @@ static int64_t leading_rows(int64_t M, int64_t N, int64_t K) {
   return M1;
 }
 
+int gemm_parts(int64_t M, int64_t N, int64_t K, GemmPart parts[2]) {
+  const int64_t M1 = leading_rows(M, N, K);
+  if (M1 > 0) {
+    parts[0] = GemmPart{0, M1, 1};
+    parts[1] = GemmPart{M1, M - M1, choose_splits(M - M1, N, K)};
+    return 2;
+  }
+  parts[0] = GemmPart{0, M, choose_splits(M, N, K)};
+  return 1;
+}
+
+size_t part_workspace(const GemmPart& p, int64_t N) {
+  return p.splits > 1 ? (size_t)p.splits * (size_t)p.rows * (size_t)N * 4 : 0;
+}
+
+// The workspace of a call (puro_fp8_gemm, puro_fp8_gemm_accumulate and puro_fp8_gemm_quant follow
+// the same plan): its largest part.
+size_t gemm_workspace_bytes(int, int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || K <= 0) return 0;
+  GemmPart parts[2];
+  const int n = gemm_parts(M, N, K, parts);
+  size_t need = 0;
+  for (int i = 0; i < n; ++i) need = std::max(need, part_workspace(parts[i], N));
+  return need;
+}
+
 hipError_t launch_gemm(int mode, int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
                        const float* sA, const uint8_t* B, int64_t ldb, const float* sB, void* C,
                        int64_t ldc, bool out_bf16, bool accumulate, uint8_t* q, int64_t ldq, float* qs,
@@ -632,20 +654,25 @@ hipError_t launch_gemm(int mode, int64_t M, int64_t N, int64_t K, const uint8_t*
     hipLaunchKernelGGL(zero_fill_kernel, dim3(8, (unsigned)gy), dim3(256), 0, st, C, M, N * es, ldc * es);
     return hipGetLastError();
   }
-  // (the fused output quantization writes its scales with stride M: no row ranges there)
-  const int64_t M1 = q == nullptr ? leading_rows(M, N, K) : 0;
-  if (M1 > 0) {
-    const int64_t es = out_bf16 ? 2 : 4;
-    hipError_t e = launch_rows(mode, M1, N, K, A, lda, sA, M, B, ldb, sB, C, ldc, out_bf16, accumulate, nullptr, 0,
-                               nullptr, workspace, workspace_bytes, st);
-    if (e != hipSuccess) return e;
-    // sA (and the MX E8M0 tiles, 4 bytes per row) of row M1 start M1 elements in
-    return launch_rows(mode, M - M1, N, K, A + M1 * lda, lda, sA + M1, M, B, ldb, sB,
-                       static_cast<uint8_t*>(C) + M1 * ldc * es, ldc, out_bf16, accumulate, nullptr, 0, nullptr,
-                       workspace, workspace_bytes, st);
+  GemmPart parts[2];
+  const int n = gemm_parts(M, N, K, parts);
+  // every part's workspace is checked before the first launch: a failed call writes nothing
+  for (int i = 0; i < n; ++i) {
+    const size_t need = part_workspace(parts[i], N);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return hipErrorInvalidValue;
   }
-  return launch_rows(mode, M, N, K, A, lda, sA, M, B, ldb, sB, C, ldc, out_bf16, accumulate, q, ldq, qs, workspace,
-                     workspace_bytes, st);
+  const int64_t es = out_bf16 ? 2 : 4;
+  for (int i = 0; i < n; ++i) {
+    const GemmPart& pt = parts[i];
+    // sA (and the MX E8M0 tiles, 4 bytes per row) and the output scales of row r start r elements in
+    const hipError_t e =
+        launch_rows(mode, pt.rows, N, K, pt.splits, A + pt.row0 * lda, lda, sA + pt.row0, M, B, ldb, sB,
+                    static_cast<uint8_t*>(C) + pt.row0 * ldc * es, ldc, out_bf16, accumulate,
+                    q ? q + pt.row0 * ldq : nullptr, ldq, q ? qs + pt.row0 : nullptr, M, workspace,
+                    workspace_bytes, st);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace puro

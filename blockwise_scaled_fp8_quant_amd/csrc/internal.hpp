@@ -8,8 +8,9 @@
 
 namespace puro {
 
+// s[kb * lds + m] is the scale of row m, group kb; lds = 0 means M (the public layout).
 hipError_t launch_quant_1x128(const void* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
-                              int64_t ldq, float* s, hipStream_t st);
+                              int64_t ldq, float* s, hipStream_t st, int64_t lds = 0);
 hipError_t launch_quant_128x1(const void* x, int64_t T, int64_t C, int64_t ldx, uint8_t* qT,
                               int64_t ldqT, float* sT, hipStream_t st);
 hipError_t launch_quant_dual(const void* x, int64_t T, int64_t C, int64_t ldx, uint8_t* q, int64_t ldq,
@@ -47,6 +48,16 @@ hipError_t launch_quant_128x128_batch(const WeightJob* jobs, int n, hipStream_t 
 // C; q / ldq / qs (bf16 output only, optional) also write the 1x128 quantization of the bf16
 // C along N (codes [M, N], scales [N/128][M]).
 size_t gemm_workspace_bytes(int mode, int64_t M, int64_t N, int64_t K);
+
+// The launches of one GEMM call, in order: part p covers rows row0 .. row0 + rows - 1 of A and C
+// with the contraction split into `splits` ranges (1 = unsplit).  Returns the number of parts
+// (1 or 2); gemm_workspace_bytes is the largest part_workspace of the plan.
+struct GemmPart {
+  int64_t row0, rows;
+  int splits;
+};
+int gemm_parts(int64_t M, int64_t N, int64_t K, GemmPart parts[2]);
+size_t part_workspace(const GemmPart& p, int64_t N);
 hipError_t launch_gemm(int mode, int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
                        const float* sA, const uint8_t* B, int64_t ldb, const float* sB, void* C,
                        int64_t ldc, bool out_bf16, bool accumulate, uint8_t* q, int64_t ldq, float* qs,

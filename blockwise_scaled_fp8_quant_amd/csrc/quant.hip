@@ -25,7 +25,7 @@ template <int U>
 __global__ __launch_bounds__(256) void quant_1x128_kernel(const uint16_t* __restrict__ x, int64_t M,
                                                           int G, int64_t ldx, uint8_t* __restrict__ q,
                                                           int64_t ldq, float* __restrict__ s,
-                                                          int nkbb) {
+                                                          int64_t lds, int nkbb) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int ro = lane >> 4;
@@ -41,7 +41,7 @@ __global__ __launch_bounds__(256) void quant_1x128_kernel(const uint16_t* __rest
   for (int u = 0; u < U; ++u) {
     const int kb = kb0 + u;
     if (row_ok && kb < G)
-      v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xr + kb * 128));
+      v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xr + (int64_t)kb * 128));
     else
       v[u] = u32x4{0u, 0u, 0u, 0u};
   }
@@ -57,8 +57,8 @@ __global__ __launch_bounds__(256) void quant_1x128_kernel(const uint16_t* __rest
     o.x = cvt4(bf16_lo(v[u].x) * r, bf16_hi(v[u].x) * r, bf16_lo(v[u].y) * r, bf16_hi(v[u].y) * r);
     o.y = cvt4(bf16_lo(v[u].z) * r, bf16_hi(v[u].z) * r, bf16_lo(v[u].w) * r, bf16_hi(v[u].w) * r);
     if (row_ok && kb < G) {
-      __builtin_nontemporal_store(o, reinterpret_cast<u32x2*>(qr + kb * 128));
-      if (c == 0) s[(int64_t)kb * M + row] = sc;
+      __builtin_nontemporal_store(o, reinterpret_cast<u32x2*>(qr + (int64_t)kb * 128));
+      if (c == 0) s[(int64_t)kb * lds + row] = sc;
     }
   }
 }
@@ -545,7 +545,7 @@ __global__ __launch_bounds__(256) void cast_e4m3_kernel(const float* __restrict_
 // Host-side launchers (shapes already validated by the ABI layer).
 // ---------------------------------------------------------------------------------------
 hipError_t launch_quant_1x128(const void* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
-                              int64_t ldq, float* s, hipStream_t st) {
+                              int64_t ldq, float* s, hipStream_t st, int64_t lds) {
   constexpr int U = 4;
   const int G = (int)(K / 128);
   const int nkbb = (G + U - 1) / U;
@@ -553,7 +553,7 @@ hipError_t launch_quant_1x128(const void* x, int64_t M, int64_t K, int64_t ldx, 
   const int64_t blocks = nrb * nkbb;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(quant_1x128_kernel<U>, dim3((unsigned)blocks), dim3(256), 0, st,
-                     static_cast<const uint16_t*>(x), M, G, ldx, q, ldq, s, nkbb);
+                     static_cast<const uint16_t*>(x), M, G, ldx, q, ldq, s, lds > 0 ? lds : M, nkbb);
   return hipGetLastError();
 }
 

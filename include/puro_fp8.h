@@ -158,8 +158,12 @@ int puro_fp8_quant_w_128x128_batch(const puro_fp8_wq_job* jobs, int n_jobs, hipS
  *         sB: FWD/DGRAD fp32 [N/128][K/128] (128x128 blocks); WGRAD fp32 [K/128][N].
  *   C   : [M, N] bf16 (out_dtype PURO_OUT_BF16) or fp32 (PURO_OUT_FP32), row stride ldc
  *         (elements).  M, N, K must be multiples of 128 (else PURO_ERR_SHAPE).
+ *         lda and ldb must not exceed 2^29 bytes (else PURO_ERR_UNSUPPORTED).
  *   workspace / workspace_bytes: scratch the caller provides; must be at least
  *         puro_fp8_gemm_workspace_size(mode, M, N, K) bytes (may be NULL when that is 0).
+ *         That size covers every launch the call makes (a call may run its leading rows
+ *         unsplit and the rest with a contraction split); it is checked in full before the
+ *         first launch, so a too-small workspace fails with nothing written.
  *   The summation order inside the GEMM is not part of the contract.
  */
 int puro_fp8_gemm(int mode, int64_t M, int64_t N, int64_t K,
@@ -197,7 +201,8 @@ int puro_fp8_gemm_quant(int mode, int64_t M, int64_t N, int64_t K,
                         void* C, int64_t ldc, uint8_t* q, int64_t ldq, float* s,
                         void* workspace, size_t workspace_bytes, hipStream_t st);
 
-/* Bytes of workspace puro_fp8_gemm, puro_fp8_gemm_accumulate and puro_fp8_gemm_quant need (0 = none). */
+/* Bytes of workspace puro_fp8_gemm, puro_fp8_gemm_accumulate and puro_fp8_gemm_quant need (0 = none):
+ * the largest fp32 partial-sum buffer of any launch the call makes. */
 size_t puro_fp8_gemm_workspace_size(int mode, int64_t M, int64_t N, int64_t K);
 
 /*

@@ -145,6 +145,14 @@ def test_gemm_validation_fp32_ld_rule():
     assert gm(ldc=258, dt=1) == LD
 
 
+def test_gemm_row_stride_limit():
+    # each lane's copy offset within an 8-row group, 7 ld + 127, is formed in 32 bits
+    big = 1 << 29
+    assert gm(lda=big + 16, K=256) == UNSUP and gm(ldb=big + 16) == UNSUP
+    assert ga(lda=big + 16) == UNSUP and gq(ldb=big + 16) == UNSUP
+    assert mg(lda=big + 16) == UNSUP
+
+
 def test_gemm_workspace_validation():
     # a long contraction over few tiles needs a workspace; without one the call is refused
     need = P.puro_fp8_gemm_workspace_size(2, 2048, 2048, 16384)
@@ -168,6 +176,7 @@ def test_gemm_accumulate_validation():
     # same checks as puro_fp8_gemm with an fp32 C (ld rule in 4-byte elements)
     assert ga(M=0) == OK and ga(N=0) == OK
     assert ga(mode=5) == MODE
+    assert ga(mode=3) == MODE            # the internal MX mode has no accumulating entry point
     assert ga(M=200) == SHAPE and ga(K=-128) == SHAPE
     assert ga(C=None) == NULLPTR and ga(B=None) == NULLPTR
     assert ga(C=MIS) == ALIGN and ga(sB=A16 + 8) == ALIGN

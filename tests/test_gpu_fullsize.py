@@ -215,6 +215,54 @@ def test_gemm_row_split_sampled(P):
     assert (diff <= TIGHT * den).all()
 
 
+def test_gemm_row_split_with_exactly_the_documented_workspace(P):
+    """A shape whose remaining rows need a larger contraction split than the whole problem
+    (2816 x 8192 x 32768 WGRAD: 2048 unsplit rows, then 768 rows split 8 ways): the call runs
+    with a workspace of exactly puro_fp8_gemm_workspace_size bytes, and sampled rows of both
+    parts are within the GEMM bar."""
+    t = torch()
+    M, N, K = 2816, 8192, 32768
+    need = P.puro_fp8_gemm_workspace_size(P.WGRAD, M, N, K)
+    say(f"[row split exact workspace] WGRAD M,N,K={M},{N},{K} workspace {need} B")
+    assert need >= 8 * 768 * N * 4
+    A, sA, B, sB = gemm_case("WGRAD", M, N, K, 91)
+    ws = t.empty(need, dtype=t.uint8, device="cuda")
+    C = P.puro_fp8_gemm(P.WGRAD, A, sA, B, sB, out_dtype=P.OUT_FP32, workspace=ws)
+    t.cuda.synchronize()
+    rng = np.random.default_rng(92)
+    rows = np.sort(np.concatenate([rng.choice(2048, size=32, replace=False), 2048 + rng.choice(768, size=32, replace=False)]))
+    cols = np.sort(rng.choice(N, size=48, replace=False))
+    rt, ct = t.from_numpy(rows).cuda(), t.from_numpy(cols).cuda()
+    Ad = gemm.dequant_a(host(A[rt]), host(sA[:, rt]))
+    Bd = gemm.dequant_b("WGRAD", host(B[ct]), host(sB[:, ct]))
+    ref = Ad @ Bd.T
+    err, diff, den = normalized_error(host(C[rt][:, ct]), ref, np.sqrt((Ad * Ad).sum(1)), np.sqrt((Bd * Bd).sum(1)))
+    say(f"    max normalized error {err:.3e}")
+    assert (diff <= TIGHT * den).all()
+
+
+def test_gemm_quant_row_split(P):
+    """The fused output quantization on a two-part plan (8192 unsplit rows, 256 rows split): C, codes
+    and scales equal GEMM-then-quantize everywhere, and sampled 128-row blocks of both parts equal
+    the oracle's 1x128 quantizer on the bf16 C."""
+    t = torch()
+    M, N, K = ROW_SPLIT
+    say(f"[row split gemm quant] WGRAD M,N,K={M},{N},{K}")
+    A, sA, B, sB = gemm_case("WGRAD", M, N, K, 93)
+    C, q, s = P.puro_fp8_gemm_quant(P.WGRAD, A, sA, B, sB)
+    C2 = P.puro_fp8_gemm(P.WGRAD, A, sA, B, sB, out_dtype=P.OUT_BF16)
+    q2, s2 = P.puro_fp8_quant_act_1x128(C2)
+    t.cuda.synchronize()
+    assert bool((C.view(t.int16) == C2.view(t.int16)).all())
+    assert bool((q == q2).all())
+    assert bool((s.view(t.int32) == s2.view(t.int32)).all())
+    for rb in (3, 63, 64, 65):                       # blocks 64 and 65 lie in the split part
+        rows = slice(128 * rb, 128 * rb + 128)
+        rq, rs = quant.quant_act_1x128(bits_of(C[rows]))
+        assert_bytes_equal(host(q[rows]), rq, f"codes of rows {128 * rb}..")
+        assert_bytes_equal(host(s[:, rows]), rs, f"scales of rows {128 * rb}..")
+
+
 def test_mx_gemm_row_split_sampled(P):
     from oracle import mx
     t = torch()

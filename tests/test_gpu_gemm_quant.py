@@ -1,9 +1,14 @@
 """GPU tests of puro_fp8_gemm_quant: the GEMM with the 1x128 quantization of its bf16 output
 fused into the epilogue.
 
-Bars: (C, q, s) byte-identical to puro_fp8_gemm's bf16 C followed by puro_fp8_quant_act_1x128(C)
-(the unfused path, whose quantizer is bit-exact against the oracle); C within the GEMM bar
-against the oracle; q, s reconstruct C within the quantizer's own error bound.
+Bars:
+  - q, s byte-identical to the oracle's 1x128 quantizer (oracle.quant.quant_act_1x128) applied
+    to the bf16 bits of the C the kernel wrote (everywhere on small shapes, on sampled 128-row
+    blocks at full size): the fused epilogue quantizes the output it writes;
+  - (C, q, s) byte-identical to puro_fp8_gemm's bf16 C followed by puro_fp8_quant_act_1x128(C)
+    (the unfused path);
+  - C within the GEMM bar against the oracle; q, s reconstruct C within the quantizer's own
+    error bound.
 """
 import numpy as np
 import pytest
@@ -37,6 +42,11 @@ def operands(mode, M, N, K, seed):
     return A, sA, B, sB
 
 
+def bf16_bits(c_f32: np.ndarray) -> np.ndarray:
+    """uint16 bf16 bit patterns of values that came back from a bf16 tensor (exact in fp32)."""
+    return (np.ascontiguousarray(c_f32, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
 def fused_vs_unfused(P, mode, M, N, K, seed, ldc_pad=0, ldq_pad=0, check_oracle=True):
     t = torch()
     say(f"[gemm quant] {mode} M,N,K={M},{N},{K} splits={'yes' if P.puro_fp8_gemm_workspace_size(P.MODE_NAMES[mode], M, N, K) else 'no'}")
@@ -51,6 +61,10 @@ def fused_vs_unfused(P, mode, M, N, K, seed, ldc_pad=0, ldq_pad=0, check_oracle=
     C, qh = host(Cb), host(qb)
     if ldq_pad:
         assert (qh[:, N:] == 0xA5).all(), "write outside a row of q"
+    # the oracle's quantizer on the bf16 output the kernel wrote
+    rq, rs = quant.quant_act_1x128(bf16_bits(C[:, :N]))
+    assert_bytes_equal(qh[:, :N], rq, "codes vs oracle")
+    assert_bytes_equal(host(s), rs, "scales vs oracle")
     assert_bytes_equal(C[:, :N], host(C2), "C")
     assert_bytes_equal(qh[:, :N], host(q2), "codes")
     assert_bytes_equal(host(s), host(s2), "scales")
@@ -94,8 +108,9 @@ def test_gemm_quant_empty_contraction(P):
 
 @pytest.mark.parametrize("M,N,K", [(16384, 12288, 2048), (16384, 4096, 2048)])
 def test_gemm_quant_full_size(P, M, N, K):
-    """At the sweep's FWD shapes: fused == unfused on every byte (the oracle check is skipped at
-    this size; C's parity at these shapes is covered by the full-size sampled GEMM tests)."""
+    """At the sweep's FWD shapes: fused == unfused on every byte, and the fused codes and scales of
+    sampled 128-row blocks byte-identical to the oracle's quantizer on those rows of the bf16 C
+    (C's own parity at these shapes is covered by the full-size sampled GEMM tests)."""
     t = torch()
     say(f"[gemm quant full size] FWD {M}x{N}x{K}")
     g = t.Generator(device="cuda")
@@ -111,3 +126,10 @@ def test_gemm_quant_full_size(P, M, N, K):
     assert bool((C.view(t.int16) == C2.view(t.int16)).all())
     assert bool((q == q2).all())
     assert bool((s.view(t.int32) == s2.view(t.int32)).all())
+    rng = np.random.default_rng(M + N + K)
+    for rb in sorted(rng.choice(M // 128, size=3, replace=False).tolist()):
+        rows = slice(128 * rb, 128 * rb + 128)
+        cb = C[rows].contiguous().view(t.int16).cpu().numpy().view(np.uint16)
+        rq, rs = quant.quant_act_1x128(cb)
+        assert_bytes_equal(q[rows].cpu().numpy(), rq, f"codes of rows {128 * rb}.. vs oracle")
+        assert_bytes_equal(s[:, rows].contiguous().cpu().numpy(), rs, f"scales of rows {128 * rb}.. vs oracle")
