@@ -23,12 +23,13 @@ __all__ = [
     "puro_fp8_quant_w_128x128", "puro_fp8_gemm", "puro_fp8_gemm_accumulate", "puro_fp8_gemm_workspace_size",
     "puro_fp8_cast_e4m3", "puro_fp8_strerror", "puro_fp8_version", "EXPORTED_SYMBOLS",
     "puro_fp8_mx_quant_dual", "puro_fp8_mx_gemm", "puro_fp8_mx_gemm_workspace_size", "puro_fp8_gemm_quant",
-    "puro_fp8_quant_w_128x128_batch",
+    "puro_fp8_quant_w_128x128_batch", "puro_fp8_gemm_noalloc", "SCRATCH_BYTES",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpuro_fp8.so")
 
 FWD, DGRAD, WGRAD = 0, 1, 2
+SCRATCH_BYTES = 64 * 1024 * 1024   # PURO_FP8_SCRATCH_BYTES: the allocation-free GEMM's own buffer
 OUT_BF16, OUT_FP32 = 0, 1
 MODE_NAMES = {"FWD": FWD, "DGRAD": DGRAD, "WGRAD": WGRAD}
 
@@ -37,7 +38,7 @@ EXPORTED_SYMBOLS = (
     "puro_fp8_gemm", "puro_fp8_gemm_accumulate", "puro_fp8_gemm_workspace_size", "puro_fp8_cast_e4m3",
     "puro_fp8_strerror", "puro_fp8_version",
     "puro_fp8_mx_quant_dual", "puro_fp8_mx_gemm", "puro_fp8_mx_gemm_workspace_size", "puro_fp8_gemm_quant",
-    "puro_fp8_quant_w_128x128_batch",
+    "puro_fp8_quant_w_128x128_batch", "puro_fp8_gemm_noalloc",
 )
 
 if not os.path.exists(LIB_PATH):
@@ -82,6 +83,7 @@ class WqJob(ctypes.Structure):
 lib.puro_fp8_quant_w_128x128_batch.argtypes = [ctypes.POINTER(WqJob), _int, _p]
 lib.puro_fp8_gemm.argtypes = [_int, _i64, _i64, _i64, _p, _i64, _p, _p, _i64, _p, _p, _i64, _int, _p, _sz, _p]
 lib.puro_fp8_gemm_accumulate.argtypes = [_int, _i64, _i64, _i64, _p, _i64, _p, _p, _i64, _p, _p, _i64, _p, _sz, _p]
+lib.puro_fp8_gemm_noalloc.argtypes = [_int, _i64, _i64, _i64, _p, _i64, _p, _p, _i64, _p, _p, _i64, _int, _p]
 lib.puro_fp8_gemm_quant.argtypes = [_int, _i64, _i64, _i64, _p, _i64, _p, _p, _i64, _p, _p, _i64, _p, _i64, _p, _p, _sz, _p]
 lib.puro_fp8_mx_quant_dual.argtypes = [_p, _i64, _i64, _i64, _p, _i64, _p, _p, _i64, _p, _p]
 lib.puro_fp8_mx_gemm.argtypes = [_i64, _i64, _i64, _p, _i64, _p, _p, _i64, _p, _p, _i64, _int, _p, _sz, _p]
@@ -95,7 +97,8 @@ lib.puro_fp8_strerror.restype = ctypes.c_char_p
 lib.puro_fp8_version.argtypes = []
 for _f in ("puro_fp8_quant_act_1x128", "puro_fp8_quant_act_128x1", "puro_fp8_quant_act_dual",
            "puro_fp8_quant_w_128x128", "puro_fp8_quant_w_128x128_batch", "puro_fp8_gemm",
-           "puro_fp8_gemm_accumulate", "puro_fp8_gemm_quant", "puro_fp8_mx_quant_dual", "puro_fp8_mx_gemm",
+           "puro_fp8_gemm_accumulate", "puro_fp8_gemm_quant", "puro_fp8_gemm_noalloc", "puro_fp8_mx_quant_dual",
+           "puro_fp8_mx_gemm",
            "puro_fp8_cast_e4m3", "puro_fp8_version"):
     getattr(lib, _f).restype = _int
 
@@ -324,6 +327,19 @@ def puro_fp8_gemm(mode, A, sA, B, sB, C=None, out_dtype: int = OUT_BF16, workspa
                                                lambda m, n, k: lib.puro_fp8_gemm_workspace_size(mode, m, n, k))
     _check(lib.puro_fp8_gemm(mode, M, N, K, _ptr(A), _ld(A), _ptr(sA), _ptr(B), _ld(B), _ptr(sB), _ptr(C), _ld(C),
                              out_dtype, _ptr(workspace), wbytes, _stream(stream)), "puro_fp8_gemm")
+    return C
+
+
+def puro_fp8_gemm_noalloc(mode, A, sA, B, sB, C, out_dtype: int = OUT_BF16, stream=None):
+    """puro_fp8_gemm into the caller's C without a workspace: a contraction split keeps its partial
+    sums in the library's own device buffer (SCRATCH_BYTES per device, shared by every call on the
+    device).  Neither this function nor the library allocates anything."""
+    mode = _mode(mode)
+    if C is None:
+        raise ValueError("C: the allocation-free GEMM writes into a tensor the caller provides")
+    M, N, K, C, _, _ = _gemm_args(mode, A, sA, B, sB, C, _out_dtype(out_dtype), None, lambda m, n, k: 0)
+    _check(lib.puro_fp8_gemm_noalloc(mode, M, N, K, _ptr(A), _ld(A), _ptr(sA), _ptr(B), _ld(B), _ptr(sB), _ptr(C),
+                                     _ld(C), out_dtype, _stream(stream)), "puro_fp8_gemm_noalloc")
     return C
 
 

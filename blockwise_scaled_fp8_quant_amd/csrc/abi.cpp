@@ -107,10 +107,15 @@ int puro_fp8_quant_w_128x128_batch(const puro_fp8_wq_job* jobs, int n_jobs, hipS
   return from_hip(puro::launch_quant_128x128_batch(b, n_jobs, st));
 }
 
+static_assert(PURO_FP8_SCRATCH_BYTES == puro::kScratchBytes, "the header's scratch size is the library's");
+
+// use_scratch: the library's own device buffer replaces the caller's workspace (allocation-free
+// entry point); a problem whose partials exceed it is refused before any HIP call.
 static int gemm_common(int mode, int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda, const float* sA,
                        const uint8_t* B, int64_t ldb, const float* sB, void* C, int64_t ldc, int out_dtype,
                        bool accumulate, void* workspace, size_t workspace_bytes, hipStream_t st,
-                       bool quant = false, uint8_t* q = nullptr, int64_t ldq = 0, float* qs = nullptr) {
+                       bool quant = false, uint8_t* q = nullptr, int64_t ldq = 0, float* qs = nullptr,
+                       bool use_scratch = false) {
   if (mode != PURO_GEMM_FWD && mode != PURO_GEMM_DGRAD && mode != PURO_GEMM_WGRAD && mode != kModeMx)
     return PURO_ERR_MODE;
   if (out_dtype != PURO_OUT_BF16 && out_dtype != PURO_OUT_FP32) return PURO_ERR_DTYPE;
@@ -134,6 +139,15 @@ static int gemm_common(int mode, int64_t M, int64_t N, int64_t K, const uint8_t*
   if (M > kIntMax || N > kIntMax || K > kIntMax) return PURO_ERR_UNSUPPORTED;
   if (K > 0 && (lda > kMaxGemmLd || ldb > kMaxGemmLd)) return PURO_ERR_UNSUPPORTED;
   const size_t need = puro::gemm_workspace_bytes(mode, M, N, K);
+  if (use_scratch) {
+    if (need > puro::kScratchBytes) return PURO_ERR_WORKSPACE;
+    workspace = nullptr;
+    workspace_bytes = 0;
+    if (need > 0) {
+      if (puro::scratch_buffer(&workspace) != hipSuccess) return PURO_ERR_HIP;
+      workspace_bytes = puro::kScratchBytes;
+    }
+  }
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return PURO_ERR_WORKSPACE;
   return from_hip(puro::launch_gemm(mode, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, out_dtype == PURO_OUT_BF16,
                                     accumulate, quant ? q : nullptr, ldq, qs, workspace, workspace_bytes, st));
@@ -145,6 +159,14 @@ int puro_fp8_gemm(int mode, int64_t M, int64_t N, int64_t K, const uint8_t* A, i
   if (mode == kModeMx) return PURO_ERR_MODE;   // internal mode: puro_fp8_mx_gemm
   return gemm_common(mode, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, out_dtype, false, workspace, workspace_bytes,
                      st);
+}
+
+int puro_fp8_gemm_noalloc(int mode, int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
+                          const float* sA, const uint8_t* B, int64_t ldb, const float* sB, void* C, int64_t ldc,
+                          int out_dtype, hipStream_t st) {
+  if (mode == kModeMx) return PURO_ERR_MODE;
+  return gemm_common(mode, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, out_dtype, false, nullptr, 0, st, false,
+                     nullptr, 0, nullptr, true);
 }
 
 int puro_fp8_gemm_quant(int mode, int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda, const float* sA,

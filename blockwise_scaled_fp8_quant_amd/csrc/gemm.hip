@@ -622,6 +622,30 @@ size_t part_workspace(const GemmPart& p, int64_t N) {
   return p.splits > 1 ? (size_t)p.splits * (size_t)p.rows * (size_t)N * 4 : 0;
 }
 
+// Split-K partials of the allocation-free entry point.  Uninitialized device memory, loaded with the
+// code object on each device the library runs on and kept until the process ends.  In host code
+// this name is not a device address: kernels get the address scratch_buffer looked up.
+static __device__ __attribute__((aligned(256))) uint8_t scratch[kScratchBytes];
+
+hipError_t scratch_buffer(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<void*> addr[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    // the device's own copy of the array (threads racing here all find the same address)
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev].store(p, std::memory_order_release);
+  }
+  *ptr = p;
+  return hipSuccess;
+}
+
 // The workspace of a call (puro_fp8_gemm, puro_fp8_gemm_accumulate and puro_fp8_gemm_quant follow
 // the same plan): its largest part.
 size_t gemm_workspace_bytes(int, int64_t M, int64_t N, int64_t K) {

@@ -49,6 +49,13 @@ hipError_t launch_quant_128x128_batch(const WeightJob* jobs, int n, hipStream_t 
 // C along N (codes [M, N], scales [N/128][M]).
 size_t gemm_workspace_bytes(int mode, int64_t M, int64_t N, int64_t K);
 
+// The library's own split-K buffer for callers that cannot allocate: a file-scope device array of
+// kScratchBytes per device (the same figure as PURO_FP8_SCRATCH_BYTES).  scratch_buffer returns the
+// current device's copy (its address is looked up once per device).  Every call on a device shares
+// it, so calls that overlap on one device race.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+hipError_t scratch_buffer(void** ptr);
+
 // The launches of one GEMM call, in order: part p covers rows row0 .. row0 + rows - 1 of A and C
 // with the contraction split into `splits` ranges (1 = unsplit).  Returns the number of parts
 // (1 or 2); gemm_workspace_bytes is the largest part_workspace of the plan.

@@ -201,6 +201,25 @@ int puro_fp8_gemm_quant(int mode, int64_t M, int64_t N, int64_t K,
                         void* C, int64_t ldc, uint8_t* q, int64_t ldq, float* s,
                         void* workspace, size_t workspace_bytes, hipStream_t st);
 
+/*
+ * Allocation-free puro_fp8_gemm, for callers that cannot allocate device memory or pass a
+ * workspace (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  Same arguments, layouts, result and errors as puro_fp8_gemm, except the
+ * workspace: the contraction split's fp32 partial sums go to a device buffer of
+ * PURO_FP8_SCRATCH_BYTES that the library owns, one per device, held from the library's
+ * first use on that device until the process ends.  A problem with
+ * puro_fp8_gemm_workspace_size(mode, M, N, K) > PURO_FP8_SCRATCH_BYTES is refused with
+ * PURO_ERR_WORKSPACE before anything is launched.  The call itself allocates nothing.
+ * Every call on one device shares that buffer: calls that may overlap on the same device
+ * (different streams without ordering between them) race and must be serialized by the
+ * caller.  The buffer needs no initialization; each call writes every partial it reads.
+ */
+#define PURO_FP8_SCRATCH_BYTES (64u * 1024u * 1024u)
+int puro_fp8_gemm_noalloc(int mode, int64_t M, int64_t N, int64_t K,
+                          const uint8_t* A, int64_t lda, const float* sA,
+                          const uint8_t* B, int64_t ldb, const float* sB,
+                          void* C, int64_t ldc, int out_dtype, hipStream_t st);
+
 /* Bytes of workspace puro_fp8_gemm, puro_fp8_gemm_accumulate and puro_fp8_gemm_quant need (0 = none):
  * the largest fp32 partial-sum buffer of any launch the call makes. */
 size_t puro_fp8_gemm_workspace_size(int mode, int64_t M, int64_t N, int64_t K);

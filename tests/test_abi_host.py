@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_header_and_binding_agree():
     decl = declared_functions()
-    assert len(decl) == 15
+    assert len(decl) == 16
     assert sorted(P.EXPORTED_SYMBOLS) == decl
 
 
@@ -143,6 +143,20 @@ def test_gemm_validation():
 def test_gemm_validation_fp32_ld_rule():
     # ldc * 4 must be a multiple of 16: 260 qualifies (>= N), 258 does not
     assert gm(ldc=258, dt=1) == LD
+
+
+def gn(mode=0, M=256, N=256, K=256, A=A16, lda=256, sA=A16, B=A16, ldb=256, sB=A16, C=A16, ldc=256, dt=0):
+    return P.lib.puro_fp8_gemm_noalloc(mode, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, dt, None)
+
+
+def test_gemm_noalloc_validation():
+    # the checks of puro_fp8_gemm; partials beyond the library's own buffer are refused
+    assert gn(M=0) == OK and gn(N=0) == OK
+    assert gn(mode=3) == MODE and gn(mode=9) == MODE and gn(dt=4) == DTYPE
+    assert gn(M=200) == SHAPE and gn(C=None) == NULLPTR and gn(B=MIS) == ALIGN and gn(ldc=100) == LD
+    M, N, K = 3072, 4096, 65536
+    assert P.puro_fp8_gemm_workspace_size(2, M, N, K) > P.SCRATCH_BYTES
+    assert gn(mode=2, M=M, N=N, K=K, lda=K, ldb=K, ldc=N, dt=1) == WORKSPACE
 
 
 def test_gemm_row_stride_limit():
