@@ -22,7 +22,7 @@ OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpuro_fp8.so")
 ARCH = "gfx950"
 
-SOURCES = ["quant.hip", "gemm.hip", "abi.cpp"]
+SOURCES = ["quant.hip", "gemm.hip", "gemm_w4.hip", "abi.cpp"]
 
 
 def _hipcc() -> str:

@@ -38,6 +38,7 @@
 #include <atomic>
 
 #include "codec.hpp"
+#include "gemm_args.hpp"
 #include "internal.hpp"
 #include "gemm_slice_asm.inc"
 
@@ -45,9 +46,6 @@ namespace puro {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
-typedef uint32_t g_u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t g_u32x2 __attribute__((ext_vector_type(2)));
-typedef float g_f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) void glb_void;
 
@@ -62,14 +60,6 @@ constexpr int kStageBytes = kStageA + kStageB + 1024 + 1024;   // + sA tile + sB
 // Zero scale operands select the unscaled instruction.
 __device__ __forceinline__ v16f mfma_32x32x64_e4m3(v8i x, v8i y, v16f c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(x, y, c, 0, 0, 0, 0, 0, 0);
-}
-
-// Two fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32), packed low | high << 16.
-typedef __bf16 g_bf16x2 __attribute__((ext_vector_type(2)));
-typedef float g_f32x2 __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
-  const g_f32x2 v = {lo, hi};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, g_bf16x2));
 }
 
 __device__ __forceinline__ v8i join(g_u32x4 a, g_u32x4 b) {
@@ -89,49 +79,6 @@ __device__ __forceinline__ void g2lds16(const void* g, void* lds) {
 }
 __device__ __forceinline__ void g2lds4(const void* g, void* lds) {
   __builtin_amdgcn_global_load_lds((glb_void*)g, (lds_void*)lds, 4, 0, 0);
-}
-
-struct GemmArgs {
-  int M, N, K;
-  int tiles_m, tiles_n;
-  int group;             // tile rows walked together (see tile_of)
-  int splits;            // contraction split: block b works on split b / (tiles_m * tiles_n)
-  int kb_per_split;      // 128-deep slices per split
-  int64_t split_stride;  // elements between the fp32 partial outputs of consecutive splits
-  const uint8_t* A;
-  int64_t lda;
-  const float* sA;
-  int64_t ldsa;          // elements (MX: 4-byte rows) between consecutive slices of sA: M, or the
-                         // full problem's M when this launch covers a range of its rows
-  const uint8_t* B;
-  int64_t ldb;
-  const float* sB;
-  void* C;
-  int64_t ldc;
-  int accumulate;        // fp32 output only: C = C + result (one fp32 add per element)
-  uint8_t* q;            // bf16 output only, optional: 1x128 quantization of C along N
-  int64_t ldq;
-  float* qs;             // its scales: qs[nb * ldqs + i] for row i, column block nb
-  int64_t ldqs;
-};
-
-// Map the linear workgroup id to a (tile_m, tile_n) pair: XCD-contiguous, grouped rows.  The
-// dispatcher places workgroup b on XCD b % 8; each XCD gets a contiguous run of the tile
-// sequence, which walks `group` tile rows at a time across all tile columns, so the A rows of
-// a group stay in that XCD's L2 while the B columns stream past (B is read by every XCD and
-// is shared through the memory-side cache).
-__device__ __forceinline__ void tile_of(int b, int tiles_m, int tiles_n, int group, int& tm, int& tn) {
-  const int nt = tiles_m * tiles_n;
-  const int full = (nt >> 3) << 3;
-  int logical = b;
-  if (b < full) logical = (b & 7) * (nt >> 3) + (b >> 3);
-  const int per_group = group * tiles_n;
-  const int g = logical / per_group;
-  const int first_m = g * group;
-  const int gsize = min(tiles_m - first_m, group);
-  const int r = logical - g * per_group;
-  tm = first_m + r % gsize;
-  tn = r / gsize;
 }
 
 // Swizzled position of 16-byte chunk c in a 128-byte LDS row r.  Consecutive row pairs
@@ -507,6 +454,13 @@ static hipError_t launch_one(const GemmArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// FWD and DGRAD (without the fused output quantization) run the four-wave kernel of gemm_w4.hip
+// wherever its 32-bit operand offsets reach (w4_supported), the eight-wave kernel elsewhere.
+#ifndef PURO_GEMM_W4
+#define PURO_GEMM_W4 1
+#endif
+constexpr bool kUseW4 = PURO_GEMM_W4 != 0;
+
 // Tile rows per group (see tile_of).  The A rows of a group take group x 256 x K bytes of
 // the XCD's 4 MB L2.  Up to K = 2048, 4 rows (2 MB) stay resident from one wave of tiles to
 // the next while the B columns stream past, and 8 rows (4 MB) would not; beyond that no
@@ -543,9 +497,10 @@ static hipError_t launch_rows(int mode, int64_t M, int64_t N, int64_t K, int spl
     a.ldc = N;
     a.split_stride = M * N;
     hipError_t e;
+    const bool w4 = kUseW4 && w4_supported(a);
     switch (mode) {
-      case 0: e = launch_one<0, false>(a, st); break;
-      case 1: e = launch_one<1, false>(a, st); break;
+      case 0: e = w4 ? launch_w4(a, false, st) : launch_one<0, false>(a, st); break;
+      case 1: e = w4 ? launch_w4(a, false, st) : launch_one<1, false>(a, st); break;
       case 2: e = launch_one<2, false>(a, st); break;
       default: e = launch_one<kModeMx, false>(a, st); break;
     }
@@ -577,6 +532,7 @@ static hipError_t launch_rows(int mode, int64_t M, int64_t N, int64_t K, int spl
       default: return hipErrorInvalidValue;
     }
   }
+  if (kUseW4 && (mode == 0 || mode == 1) && w4_supported(a)) return launch_w4(a, out_bf16, st);
   switch (mode * 2 + (out_bf16 ? 1 : 0)) {
     case 0: return launch_one<0, false>(a, st);
     case 1: return launch_one<0, true>(a, st);

@@ -1,0 +1,69 @@
+// Arguments and helpers shared by the two blockwise GEMM kernels (gemm.hip: eight waves, 64x128 wave
+// tiles, every mode; gemm_w4.hip: four waves, 128x128 wave tiles, FWD and DGRAD).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace puro {
+
+typedef uint32_t g_u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t g_u32x2 __attribute__((ext_vector_type(2)));
+typedef float g_f32x4 __attribute__((ext_vector_type(4)));
+
+// Two fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32), packed low | high << 16.
+typedef __bf16 g_bf16x2 __attribute__((ext_vector_type(2)));
+typedef float g_f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
+  const g_f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, g_bf16x2));
+}
+
+struct GemmArgs {
+  int M, N, K;
+  int tiles_m, tiles_n;
+  int group;             // tile rows walked together (see tile_of)
+  int splits;            // contraction split: block b works on split b / (tiles_m * tiles_n)
+  int kb_per_split;      // 128-deep slices per split
+  int64_t split_stride;  // elements between the fp32 partial outputs of consecutive splits
+  const uint8_t* A;
+  int64_t lda;
+  const float* sA;
+  int64_t ldsa;          // elements (MX: 4-byte rows) between consecutive slices of sA: M, or the
+                         // full problem's M when this launch covers a range of its rows
+  const uint8_t* B;
+  int64_t ldb;
+  const float* sB;
+  void* C;
+  int64_t ldc;
+  int accumulate;        // fp32 output only: C = C + result (one fp32 add per element)
+  uint8_t* q;            // bf16 output only, optional: 1x128 quantization of C along N
+  int64_t ldq;
+  float* qs;             // its scales: qs[nb * ldqs + i] for row i, column block nb
+  int64_t ldqs;
+};
+
+// Map the linear workgroup id to a (tile_m, tile_n) pair: XCD-contiguous, grouped rows.  The
+// dispatcher places workgroup b on XCD b % 8; each XCD gets a contiguous run of the tile
+// sequence, which walks `group` tile rows at a time across all tile columns, so the A rows of
+// a group stay in that XCD's L2 while the B columns stream past (B is read by every XCD and
+// is shared through the memory-side cache).
+__device__ __forceinline__ void tile_of(int b, int tiles_m, int tiles_n, int group, int& tm, int& tn) {
+  const int nt = tiles_m * tiles_n;
+  const int full = (nt >> 3) << 3;
+  int logical = b;
+  if (b < full) logical = (b & 7) * (nt >> 3) + (b >> 3);
+  const int per_group = group * tiles_n;
+  const int g = logical / per_group;
+  const int first_m = g * group;
+  const int gsize = min(tiles_m - first_m, group);
+  const int r = logical - g * per_group;
+  tm = first_m + r % gsize;
+  tn = r / gsize;
+}
+
+hipError_t launch_w4(const GemmArgs& a, bool out_bf16, hipStream_t st);
+// Whether launch_w4 can take these arguments: its operand offsets are 32-bit buffer offsets.
+bool w4_supported(const GemmArgs& a);
+
+}  // namespace puro

@@ -1,0 +1,264 @@
+// gfx950 blockwise-scaled FP8 GEMM, four-wave form (FWD and DGRAD: one 128x128 weight-block scale per
+// 128 columns, so every lane's promotion scale is one value per row group and slice).
+//
+//   C[i,j] = sum_kb  sA(i,kb) * sB(j/128,kb) * P_kb[i,j],   P_kb[i,j] = sum_{k in slice kb} A[i,k] B[j,k]
+//
+// The FP8 matrix cores form each 128-deep slice product P_kb (v_mfma_f32_16x16x128_f8f6f4, E4M3 x
+// E4M3 -> fp32) and the vector ALUs add it, multiplied by the slice's two scales, into a separate fp32
+// accumulator (the fine-grained scheme of the ModelScope write-up on Puro-2B, section 精度).
+//
+// One workgroup = 4 waves, one per SIMD, owns a 256x256 output tile; wave w (wm = w / 2, wn = w % 2)
+// owns the 128x128 quadrant at rows 128 wm, columns 128 wn.  At one wave per SIMD a wave has 256
+// VGPRs and 256 AGPRs: the operand fragments of a slice sit in AGPRs (the MFMA reads them there),
+// 7/8 of the accumulator in VGPRs and its last column group in AGPRs.  Each slice a wave reads
+// 128 + 128 rows of 128 bytes from LDS for 2 * 128 * 128 * 128 flops: a third less LDS read traffic
+// per flop than two waves per SIMD with 64x128 tiles.  The slice's instruction sequence is
+// generated (gen_w4_asm.py -> gemm_w4_asm.inc; register map and schedule are described there);
+// this file sets up its operands, runs the K loop over it and writes the tile out.
+//
+//  * K loop over 128-deep slices, double-buffered in LDS: while one stage is multiplied, the next
+//    slice's A and B rows (256 x 128 bytes each) and scales are copied into the other with
+//    buffer_load ... lds (no VGPR round trip).  The buffer resources span the tile's valid rows, so
+//    rows past M or N read as zero (half-filled edge tiles need no clamping).
+//  * Tiles are visited in the XCD-aware order of tile_of (gemm_args.hpp).
+//  * The epilogue stages each wave's quadrant through LDS, 64 rows at a time, and writes whole
+//    row segments with 16-byte stores.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+
+#include "gemm_args.hpp"
+#include "gemm_w4_asm.inc"
+#include "internal.hpp"
+
+namespace puro {
+
+namespace {
+
+typedef int w4_v4i __attribute__((ext_vector_type(4)));
+typedef int w4_v8i __attribute__((ext_vector_type(8)));
+typedef float w4_v2f __attribute__((ext_vector_type(2)));
+typedef float w4_v4f __attribute__((ext_vector_type(4)));
+typedef float w4_v16f __attribute__((ext_vector_type(16)));
+
+constexpr int kW4Threads = 256;
+// 2 stages x (A 32 KB + B 32 KB), 2 stages x 2 KB of scales, 256 bytes that the L2 prefetches land in
+constexpr int kW4Lds = 131072 + 2 * 2048 + 256;
+constexpr uint32_t kRsrcWord3 = 0x00020000u; // raw buffer, 32-bit data format (gfx9 family)
+
+// Buffer resource of `bytes` bytes at `base` (stride 0: a plain byte range; reads past it return 0).
+__device__ __forceinline__ w4_v4i rsrc(const void* base, int64_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint64_t n = bytes < 0 ? 0 : (bytes > 0xFFFFFFFFll ? 0xFFFFFFFFull : (uint64_t)bytes);
+  w4_v4i r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)((a >> 32) & 0xFFFFu));
+  r[2] = __builtin_amdgcn_readfirstlane((int)(uint32_t)n);
+  r[3] = (int)kRsrcWord3;
+  return r;
+}
+
+}  // namespace
+
+template <bool OUT_BF16>
+__global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm_w4_kernel(GemmArgs p) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  int tm, tn;
+  const int ntiles = p.tiles_m * p.tiles_n;
+  const int split = blockIdx.x / ntiles;
+  tile_of(blockIdx.x - split * ntiles, p.tiles_m, p.tiles_n, p.group, tm, tn);
+  const int m0 = tm * 256, n0 = tn * 256;
+  const int nk = p.K / 128;
+  const int kb_begin = split * p.kb_per_split;
+  const int kb_end = min(kb_begin + p.kb_per_split, nk);
+
+  // ---- copy operands (see gen_w4_asm.py): buffer resources over the tile's valid rows
+  const w4_v4i rA = rsrc(p.A + (int64_t)m0 * p.lda, (int64_t)min(256, p.M - m0) * p.lda);
+  const w4_v4i rB = rsrc(p.B + (int64_t)n0 * p.ldb, (int64_t)min(256, p.N - n0) * p.ldb);
+  const w4_v4i rS = rsrc(p.sA + m0, ((int64_t)nk * p.ldsa - m0) * 4);
+  const w4_v4i rW = rsrc(p.sB + (int64_t)(n0 >> 7) * nk, (int64_t)((p.N >> 7) - (n0 >> 7)) * nk * 4);
+  w4_v8i qa, qb;                                   // the wave's 8-row copy groups
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    qa[q] = __builtin_amdgcn_readfirstlane((int)(uint32_t)((64 * wave + 8 * q) * p.lda));
+    qb[q] = __builtin_amdgcn_readfirstlane((int)(uint32_t)((64 * wave + 8 * q) * p.ldb));
+  }
+  // the lane lands at physical chunk (lane & 7) of row r = 64 wave + 8 q + (lane >> 3) and fetches
+  // the logical chunk stored there; (r >> 1) & 7 = ((lane >> 4) + 4 q) & 7, so odd groups flip bit 2
+  const int crow = lane >> 3, pch = lane & 7;
+  const uint32_t k0 = (uint32_t)kb_begin * 128u;
+  uint32_t oa0 = (uint32_t)(crow * p.lda) + (uint32_t)((pch ^ (crow >> 1)) << 4) + k0;
+  uint32_t oa1 = (uint32_t)(crow * p.lda) + (uint32_t)((pch ^ (crow >> 1) ^ 4) << 4) + k0;
+  uint32_t ob0 = (uint32_t)(crow * p.ldb) + (uint32_t)((pch ^ (crow >> 1)) << 4) + k0;
+  uint32_t ob1 = (uint32_t)(crow * p.ldb) + (uint32_t)((pch ^ (crow >> 1) ^ 4) << 4) + k0;
+  const uint32_t osa = (uint32_t)lane * 4u;
+  // prefetch offsets: row 64 wave + lane (the wave's base row is in qa[0] / qb[0]), two slices ahead
+  // of the one being copied; the prologue prefetches the second slice
+  uint32_t pfa = (uint32_t)(lane * p.lda) + k0 + 128u;
+  uint32_t pfb = (uint32_t)(lane * p.ldb) + k0 + 128u;
+  int ssp;                                         // row-scale offset of the prefetched slice
+  int ssa = __builtin_amdgcn_readfirstlane((int)(((int64_t)kb_begin * p.ldsa + 64 * wave) * 4));
+  int ssw = __builtin_amdgcn_readfirstlane((wn * nk + kb_begin) * 4);
+  const int sstep = __builtin_amdgcn_readfirstlane((int)(p.ldsa * 4));
+  const int mw = wave * 8192, ms = 131072 + 256 * wave;
+
+  // ---- fragment read addresses (stage 0): the lane's two 16-byte chunks of its row; every row a
+  // lane reads has the swizzle term (lane & 15) >> 1 (row offsets are multiples of 16)
+  const int l16 = lane & 15, g = lane >> 4, sw = l16 >> 1;
+  const uint32_t c0 = (uint32_t)(((2 * g) ^ sw) << 4), c1 = (uint32_t)(((2 * g + 1) ^ sw) << 4);
+  const uint32_t aj0 = (uint32_t)((128 * wm + l16) * 128) + c0, aj1 = (uint32_t)((128 * wm + l16) * 128) + c1;
+  const uint32_t bj0 = 65536u + (uint32_t)((128 * wn + l16) * 128) + c0;
+  const uint32_t bj1 = 65536u + (uint32_t)((128 * wn + l16) * 128) + c1;
+  const uint32_t sj = 131072u + 4u * (uint32_t)(128 * wm + l16);
+  const uint32_t swj = 131072u + 1024u + 256u * (uint32_t)wave;
+
+  // accumulators, products, scales and temporaries: set to zero inside the K loop's asm while the
+  // first slice's copies are in flight.  They are early-clobber outputs: written while the inputs
+  // are still being read, so they never share a register with an input.
+  w4_v16f acc[14];
+  w4_v4f agp[8];                 // tiles (mi, 7): as 4-register operands
+  w4_v4f p0, p1, p2, tmp;
+  w4_v2f sc;
+
+#define PURO_W4_OUTS                                                                                         \
+  "=&{v[0:15]}"(acc[0]), "=&{v[16:31]}"(acc[1]), "=&{v[32:47]}"(acc[2]), "=&{v[48:63]}"(acc[3]),             \
+      "=&{v[64:79]}"(acc[4]), "=&{v[80:95]}"(acc[5]), "=&{v[96:111]}"(acc[6]), "=&{v[112:127]}"(acc[7]),     \
+      "=&{v[128:143]}"(acc[8]), "=&{v[144:159]}"(acc[9]), "=&{v[160:175]}"(acc[10]),                         \
+      "=&{v[176:191]}"(acc[11]), "=&{v[192:207]}"(acc[12]), "=&{v[208:223]}"(acc[13]),                       \
+      "=&{a[0:3]}"(agp[0]), "=&{a[4:7]}"(agp[1]), "=&{a[8:11]}"(agp[2]), "=&{a[12:15]}"(agp[3]),             \
+      "=&{a[16:19]}"(agp[4]), "=&{a[20:23]}"(agp[5]), "=&{a[24:27]}"(agp[6]), "=&{a[28:31]}"(agp[7]),        \
+      "=&{v[224:227]}"(p0), "=&{v[228:231]}"(p1), "=&{v[232:235]}"(p2), "=&{v[236:237]}"(sc),                \
+      "=&{v[238:241]}"(tmp), "+{v243}"(oa0), "+{v244}"(oa1), "+{v245}"(ob0), "+{v246}"(ob1), "+{v247}"(pfa), \
+      "+{v248}"(pfb), [ssa] "+s"(ssa), [ssw] "+s"(ssw), [ssp] "=&s"(ssp), [pairs] "+s"(pairs)
+#define PURO_W4_INS                                                                                         \
+  [aj0] "v"(aj0), [aj1] "v"(aj1), [bj0] "v"(bj0), [bj1] "v"(bj1), [sj] "v"(sj), [swj] "v"(swj),             \
+      [osa] "v"(osa), [rA] "s"(rA), [rB] "s"(rB), [rS] "s"(rS), [rW] "s"(rW), [qa] "{s[64:71]}"(qa),        \
+      [qb] "{s[72:79]}"(qb), [sstep] "s"(sstep), [mw] "s"(mw), [ms] "s"(ms), [rem] "s"(rem)
+#define PURO_W4_CLOB PURO_W4_CLOBBERS, "v242", "m0", "scc", "memory"
+
+  // slices kb_begin .. kb_end - 1 (at least one): `pairs` stage-0 / stage-1 pairs that copy the
+  // slice after them, then the last `rem` (1 or 2) slices
+  const int n = kb_end - kb_begin;
+  int pairs = __builtin_amdgcn_readfirstlane((n - 1) / 2);
+  const int rem = __builtin_amdgcn_readfirstlane(n - 2 * ((n - 1) / 2));
+  asm volatile(PURO_W4_MAINLOOP : PURO_W4_OUTS : PURO_W4_INS : PURO_W4_CLOB);
+  (void)ssp;
+#undef PURO_W4_OUTS
+#undef PURO_W4_INS
+#undef PURO_W4_CLOB
+
+  // ---- epilogue: each wave stages its quadrant in its own LDS region (bf16: all 128 rows, row stride
+  // 264 B; fp32: 64 rows at a time, 528 B; consecutive rows land 2 / 4 banks apart), then writes whole
+  // row segments with 16-byte stores, eight rows' reads in flight at a time.  The last slice block
+  // ended with a barrier, so LDS is free; the stores are not waited for (only the LDS reads).
+  constexpr int kEs = OUT_BF16 ? 2 : 4;
+  constexpr int kRow = 128 * kEs + (OUT_BF16 ? 8 : 16);
+  constexpr int kStaged = OUT_BF16 ? 128 : 64;           // rows staged per pass
+  constexpr int kLanesPerRow = 128 * kEs / 16;           // 16 (bf16) or 32 (fp32)
+  constexpr int kRowsPerIt = 64 / kLanesPerRow;          // rows one 16-byte store instruction covers
+  constexpr int kBatch = 8;
+  static_assert(4 * kStaged * kRow <= kW4Lds, "epilogue staging exceeds the LDS allocation");
+  uint8_t* wbuf = smem + wave * (kStaged * kRow);
+  const bool cols_ok = n0 + 128 * wn < p.N;
+  const int rr = lane / kLanesPerRow, rc = lane % kLanesPerRow;
+#pragma unroll
+  for (int h = 0; h < 128 / kStaged; ++h) {
+    constexpr int kGroups = kStaged / 16;                // row groups per pass
+#pragma unroll
+    for (int mi = kGroups * h; mi < kGroups * h + kGroups; ++mi) {
+#pragma unroll
+      for (int ni = 0; ni < 8; ++ni) {
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if (ni < 7) {
+            const int tt = 7 * mi + ni;
+            v[r] = acc[tt >> 2][4 * (tt & 3) + r];
+          } else {
+            v[r] = agp[mi][r];
+          }
+        }
+        uint8_t* dst = wbuf + (16 * (mi - kGroups * h) + l16) * kRow + (16 * ni + 4 * g) * kEs;
+        if constexpr (OUT_BF16) {
+          g_u32x2 o;
+          o[0] = bf16x2_rne(v[0], v[1]);
+          o[1] = bf16x2_rne(v[2], v[3]);
+          *reinterpret_cast<g_u32x2*>(dst) = o;
+        } else {
+          const g_f32x4 o = {v[0], v[1], v[2], v[3]};
+          *reinterpret_cast<g_f32x4*>(dst) = o;
+        }
+      }
+    }
+    // the wave reads back its own rows: wait for its LDS writes only
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_wave_barrier();
+    const int row0 = m0 + 128 * wm + kStaged * h;
+    if (row0 < p.M && cols_ok) {
+      uint8_t* cbase = static_cast<uint8_t*>(p.C) +
+                       ((int64_t)split * p.split_stride + (int64_t)row0 * p.ldc + n0 + 128 * wn) * kEs;
+#pragma unroll
+      for (int it0 = 0; it0 < kStaged / kRowsPerIt; it0 += kBatch) {
+        g_u32x4 v[kBatch];
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b)
+          v[b] = *reinterpret_cast<const g_u32x4*>(wbuf + ((it0 + b) * kRowsPerIt + rr) * kRow + rc * 16);
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b) {
+          const int r = (it0 + b) * kRowsPerIt + rr;
+          g_u32x4* cp = reinterpret_cast<g_u32x4*>(cbase + (int64_t)r * p.ldc * kEs + rc * 16);
+          g_u32x4 o = v[b];
+          if (!OUT_BF16 && p.accumulate) {
+            const g_f32x4 sum = __builtin_bit_cast(g_f32x4, o) + __builtin_bit_cast(g_f32x4, *cp);
+            o = __builtin_bit_cast(g_u32x4, sum);
+          }
+          *cp = o;
+        }
+      }
+    }
+    if (h + 1 < 128 / kStaged) {
+      // the next pass overwrites the staging area: this pass's reads must have returned
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+}
+
+// Every operand offset the kernel forms must fit the 32-bit offsets of a buffer access: A / B rows up
+// to 256 x ld bytes past the tile's first row (plus prefetches two slices beyond the last), row-scale
+// offsets up to (K / 128 + 2) slices of ldsa floats.
+bool w4_supported(const GemmArgs& a) {
+  const int64_t lim = int64_t(1) << 32;
+  const int64_t nk = a.K / 128;
+  return 256 * a.lda + 512 < lim && 256 * a.ldb + 512 < lim && (nk + 2) * a.ldsa * 4 + 1024 < lim;
+}
+
+hipError_t launch_w4(const GemmArgs& a, bool out_bf16, hipStream_t st) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<bool> attr_set[2][kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const bool known = dev >= 0 && dev < kMaxDevices;
+  const void* fn = out_bf16 ? reinterpret_cast<const void*>(&gemm_w4_kernel<true>)
+                            : reinterpret_cast<const void*>(&gemm_w4_kernel<false>);
+  if (!known || !attr_set[out_bf16][dev].load(std::memory_order_acquire)) {
+    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kW4Lds);
+    if (e != hipSuccess) return e;
+    if (known) attr_set[out_bf16][dev].store(true, std::memory_order_release);
+  }
+  const dim3 grid((unsigned)(a.tiles_m * a.tiles_n * a.splits));
+  if (out_bf16)
+    hipLaunchKernelGGL(gemm_w4_kernel<true>, grid, dim3(kW4Threads), kW4Lds, st, a);
+  else
+    hipLaunchKernelGGL(gemm_w4_kernel<false>, grid, dim3(kW4Threads), kW4Lds, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace puro
