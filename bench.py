@@ -1,9 +1,10 @@
 """Benchmark of the blockwise-scaled FP8 linear-layer hot path on one MI355X.
 
 One step = one pass of the whole path over the full-layer workload at 16384 tokens
-(4 sequences of 4096), seed 0: for each of the 4 linear weights of one ~2B-scale layer
+(4 sequences of 4096), seed 0, on the 4 linear weights of one ~2B-scale layer
 (qkv 4096x2048, o 2048x2048, gate+up 12288x2048, down 2048x6144):
-    quantize W 128x128 (+ transposed copy);
+    quantize all 4 W 128x128 (+ transposed copies) in one launch;
+  then for each weight:
     quantize X  1x128 and 128x1 in one pass (dual quantizer);  FWD   Y  = X  W^T  (bf16 out)
     quantize dY 1x128 and 128x1 in one pass (dual quantizer);  DGRAD dX = dY W    (bf16 out)
                                                                 WGRAD dW = dY^T X  (fp32 out)
@@ -17,7 +18,9 @@ standalone 1x128 and 128x1 quantizers and the FWD GEMM with its output's 1x128 q
 fused into the epilogue are timed on the same tensors (reported under `kernels` with
 "in_step": false; not part of `value`), and so is the MXFP8 variant of the
 whole step (`mx_variant`: blocks of 32 with E8M0 scales; W, X and dY through the MX dual
-quantizer, then the three GEMMs).
+quantizer, then the three GEMMs).  `configs` times the other named configurations (the tiny
+outlier case, the QKV projection FWD at 4096 tokens, the MLP FWD and the down-projection
+backward at 8192 tokens) op by op on their own seeded inputs, each launch reading from HBM.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
 
@@ -25,8 +28,8 @@ HBM traffic of each kernel comes from two rocprofv3 counter runs of this script 
 then WRITE_SIZE), both scaled by what the same counter reads for a plain copy of known size
 that every run performs once, untimed, before the steps:
 
-    rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/pmc_fetch -o pmc -- python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline
-    rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/pmc_write -o pmc -- python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline
+    rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/pmc_fetch -o pmc -- python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-configs
+    rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/pmc_write -o pmc -- python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-configs
     python bench.py --summarize-pmc OUT/pmc_fetch OUT/pmc_write   # writes TRAFFIC_FILE
 
 The summary records a hash of the kernel sources; once they change, `traffic` reads null
@@ -138,8 +141,8 @@ def summarize_pmc(fetch_dir: str, write_dir: str):
             if counter == "FETCH_SIZE" and not cont:
                 e["launches"] += 1
     lines = ["# HBM traffic per launch: layer sweep, 16384 tokens, seed 0 (bench step)",
-             "# rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/pmc_fetch -o pmc -- python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline",
-             "# rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/pmc_write -o pmc -- python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline",
+             "# rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/pmc_fetch -o pmc -- python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-configs",
+             "# rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/pmc_write -o pmc -- python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-configs",
              "# python bench.py --summarize-pmc OUT/pmc_fetch OUT/pmc_write   (OUT: the counter runs' output directory)",
              "# counters are scaled so that the calibration copy (256 MiB read + 256 MiB written) reads its own size;",
              "# a GEMM op includes its split-K reduce kernel and both launches of a row-split GEMM",
@@ -192,6 +195,7 @@ def build_step(P, torch, d):
     u8 = lambda *s: torch.empty(s, dtype=torch.uint8, device=dev)
     f32 = lambda *s: torch.empty(s, dtype=torch.float32, device=dev)
     keep = []
+    wjobs, wouts, wbytes = [], [], 0
     for wname, (dout, din) in SWEEP_WEIGHTS:
         X, W, dY = bf16(d[f"X_{wname}"]), bf16(d[f"W_{wname}"]), bf16(d[f"dY_{wname}"])
         T = X.shape[0]
@@ -208,8 +212,10 @@ def build_step(P, torch, d):
         qdb = lambda n: {"kind": "quant", "bytes": 2 * n + 2 * n + 2 * 4 * (n // 128)}
         qwb = {"kind": "quant", "bytes": 2 * dout * din + 2 * dout * din + 2 * 4 * (dout // 128) * (din // 128)}
         gf = lambda m, n, k, ob: {"kind": "gemm", "flops": 2 * m * n * k, "bytes": m * k + n * k + 4 * (m + n) * (k // 128) + ob * m * n}
+        wjobs.append(W)
+        wouts.append((Wq, Ws, WqT, WsT))
+        wbytes += qwb["bytes"]
         ops += [
-            ("quant_w_128x128", lambda W=W, Wq=Wq, Ws=Ws, WqT=WqT, WsT=WsT: P.puro_fp8_quant_w_128x128(W, Wq, Ws, WqT, WsT), qwb, wname),
             ("quant_act_dual", lambda X=X, Xq=Xq, Xs=Xs, XqT=XqT, XsT=XsT: P.puro_fp8_quant_act_dual(X, Xq, Xs, XqT, XsT), qdb(T * din), wname),
             ("gemm_fwd", lambda Xq=Xq, Xs=Xs, Wq=Wq, Ws=Ws, Y=Y: P.puro_fp8_gemm(P.FWD, Xq, Xs, Wq, Ws, C=Y, out_dtype=P.OUT_BF16), gf(T, dout, din, 2), wname),
             ("quant_act_dual", lambda dY=dY, Gq=Gq, Gs=Gs, GqT=GqT, GsT=GsT: P.puro_fp8_quant_act_dual(dY, Gq, Gs, GqT, GsT), qdb(T * dout), wname),
@@ -241,7 +247,112 @@ def build_step(P, torch, d):
             ("quant_act_128x1", lambda dY=dY, GqT=GqT, GsT=GsT: P.puro_fp8_quant_act_128x1(dY, GqT, GsT), qb(T * dout), wname),
             ("quant_act_128x1", lambda X=X, XqT=XqT, XsT=XsT: P.puro_fp8_quant_act_128x1(X, XqT, XsT), qb(T * din), wname),
         ]
+    # the four weights are quantized anew once per step (after an optimizer step), in one launch
+    ops.insert(0, ("quant_w_128x128", lambda: P.puro_fp8_quant_w_128x128_batch(wjobs, wouts),
+                   {"kind": "quant", "bytes": wbytes}, "all"))
     return ops, single, mxops, keep
+
+
+def config_ops(P, torch, name, d):
+    """The ops of one named configuration, on its own seeded inputs: [(op name, thunk, work)]."""
+    dev = "cuda:0"
+
+    def bf16(b):
+        import numpy as np
+        return torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    qb = lambda n: {"kind": "quant", "bytes": 3 * n + 4 * (n // 128)}
+    qdb = lambda n: {"kind": "quant", "bytes": 4 * n + 8 * (n // 128)}
+    qwb = lambda n, t: {"kind": "quant", "bytes": (4 if t else 3) * n + (8 if t else 4) * (n // 16384)}
+    gf = lambda m, n, k, ob: {"kind": "gemm", "flops": 2 * m * n * k, "bytes": m * k + n * k + ob * m * n}
+    ops = []
+    if name in ("tiny", "qkv_fwd"):
+        X, W = bf16(d["X"]), bf16(d["W"])
+        (T, K), N = X.shape, W.shape[0]
+        Xq, Xs = P.puro_fp8_quant_act_1x128(X)
+        Wq, Ws, _, _ = P.puro_fp8_quant_w_128x128(W, transposed=False)
+        out = P.OUT_FP32 if name == "tiny" else P.OUT_BF16
+        Y = torch.empty((T, N), dtype=torch.float32 if name == "tiny" else torch.bfloat16, device=dev)
+        ops += [("quant_act_1x128 X", lambda: P.puro_fp8_quant_act_1x128(X, Xq, Xs), qb(T * K)),
+                ("quant_w_128x128 W", lambda: P.puro_fp8_quant_w_128x128(W, Wq, Ws, transposed=False), qwb(N * K, False)),
+                ("gemm_fwd", lambda: P.puro_fp8_gemm(P.FWD, Xq, Xs, Wq, Ws, C=Y, out_dtype=out),
+                 gf(T, N, K, 4 if name == "tiny" else 2))]
+    elif name == "mlp_fwd":
+        X, Wg, H, Wd = bf16(d["X"]), bf16(d["W_gu"]), bf16(d["H"]), bf16(d["W_d"])
+        Xq, Xs = P.puro_fp8_quant_act_1x128(X)
+        Hq, Hs = P.puro_fp8_quant_act_1x128(H)
+        Wgq, Wgs, _, _ = P.puro_fp8_quant_w_128x128(Wg, transposed=False)
+        Wdq, Wds, _, _ = P.puro_fp8_quant_w_128x128(Wd, transposed=False)
+        G = torch.empty((X.shape[0], Wg.shape[0]), dtype=torch.bfloat16, device=dev)
+        Y = torch.empty((H.shape[0], Wd.shape[0]), dtype=torch.bfloat16, device=dev)
+        ops += [("quant_act_1x128 X", lambda: P.puro_fp8_quant_act_1x128(X, Xq, Xs), qb(X.numel())),
+                ("quant_w_128x128 W_gu", lambda: P.puro_fp8_quant_w_128x128(Wg, Wgq, Wgs, transposed=False), qwb(Wg.numel(), False)),
+                ("gemm_fwd gate_up", lambda: P.puro_fp8_gemm(P.FWD, Xq, Xs, Wgq, Wgs, C=G, out_dtype=P.OUT_BF16),
+                 gf(X.shape[0], Wg.shape[0], X.shape[1], 2)),
+                ("quant_act_1x128 H", lambda: P.puro_fp8_quant_act_1x128(H, Hq, Hs), qb(H.numel())),
+                ("quant_w_128x128 W_d", lambda: P.puro_fp8_quant_w_128x128(Wd, Wdq, Wds, transposed=False), qwb(Wd.numel(), False)),
+                ("gemm_fwd down", lambda: P.puro_fp8_gemm(P.FWD, Hq, Hs, Wdq, Wds, C=Y, out_dtype=P.OUT_BF16),
+                 gf(H.shape[0], Wd.shape[0], H.shape[1], 2))]
+    elif name == "down_bwd":
+        dY, Wd, H = bf16(d["dY"]), bf16(d["W_d"]), bf16(d["H"])
+        T, Dout = dY.shape
+        Din = Wd.shape[1]
+        Gq, Gs, GqT, GsT = P.puro_fp8_quant_act_dual(dY)
+        Wq, Ws, WqT, WsT = P.puro_fp8_quant_w_128x128(Wd)
+        HqT, HsT = P.puro_fp8_quant_act_128x1(H)
+        dX = torch.empty((T, Din), dtype=torch.bfloat16, device=dev)
+        dW = torch.empty((Dout, Din), dtype=torch.float32, device=dev)
+        ws = torch.empty(max(P.puro_fp8_gemm_workspace_size(P.WGRAD, Dout, Din, T), 1), dtype=torch.uint8, device=dev)
+        ops += [("quant_act_dual dY", lambda: P.puro_fp8_quant_act_dual(dY, Gq, Gs, GqT, GsT), qdb(dY.numel())),
+                ("quant_w_128x128 W_d (+T)", lambda: P.puro_fp8_quant_w_128x128(Wd, Wq, Ws, WqT, WsT), qwb(Wd.numel(), True)),
+                ("quant_act_128x1 H", lambda: P.puro_fp8_quant_act_128x1(H, HqT, HsT), qb(H.numel())),
+                ("gemm_dgrad", lambda: P.puro_fp8_gemm(P.DGRAD, Gq, Gs, WqT, WsT, C=dX, out_dtype=P.OUT_BF16),
+                 gf(T, Din, Dout, 2)),
+                ("gemm_wgrad", lambda: P.puro_fp8_gemm(P.WGRAD, GqT, GsT, HqT, HsT, C=dW, out_dtype=P.OUT_FP32, workspace=ws),
+                 gf(Dout, Din, T, 4))]
+    return ops
+
+
+def bench_configs(P, torch, iters: int):
+    """Every named configuration besides the step's (the tiny outlier case, the QKV projection FWD at
+    4096 tokens, the MLP FWD and the down-projection backward at 8192 tokens), on its own seeded
+    inputs: per op, the median over `iters` launches of its HIP-event duration, each launch after a
+    512 MiB write that evicts L2 and the memory-side cache (the op reads its inputs from HBM)."""
+    from workloads import WORKLOADS, draw
+    stream = torch.cuda.current_stream()
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda:0")
+    out = {}
+    for name in ("tiny", "qkv_fwd", "mlp_fwd", "down_bwd"):
+        d = draw(name)
+        ops = config_ops(P, torch, name, d)
+        rows = {}
+        total_us = 0.0
+        for op, fn, work in ops:
+            fn()
+            ms = []
+            for _ in range(iters):
+                flush.fill_(1)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+                e1.synchronize()
+                ms.append(e0.elapsed_time(e1))
+            us = 1000 * statistics.median(ms)
+            total_us += us
+            row = {"median_us": round(us, 2)}
+            if work["kind"] == "gemm":
+                tf = work["flops"] / (us / 1e6) / 1e12
+                row.update({"gflop": round(work["flops"] / 1e9, 2), "TFLOP/s": round(tf, 1),
+                            "frac_fp8_peak": round(tf / FP8_PEAK_TFLOPS, 4)})
+            else:
+                gbs = work["bytes"] / (us / 1e6) / 1e9
+                row.update({"alg_bytes": work["bytes"], "GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)})
+            rows[op] = row
+        out[name] = {"workload": WORKLOADS[name].note, "ops": rows, "total_us": round(total_us, 2)}
+        del ops, d
+    del flush
+    return out
 
 
 def cpu_model() -> str:
@@ -295,6 +406,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true", help="skip the other named configurations")
     ap.add_argument("--cpu-tokens", type=int, default=2048)
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     args = ap.parse_args()
@@ -414,6 +526,11 @@ def main():
                   "ms_per_step_instrumented": round(mx_inst_ms / args.steps, 4),
                   "kernels": rows(mx_per, mx_inst_ms, args.steps, True)}
 
+    configs = None
+    if not args.no_configs:
+        log("timing the other named configurations ...")
+        configs = bench_configs(P, torch, max(args.steps, 10))
+
     gemm_flops = sum(w.get("flops", 0) for _, _, w, _ in ops)
     value = gemm_flops / (ms_per_step / 1e3) / 1e12
     dom = max(per, key=lambda n: sum(per[n]["ms"]))
@@ -449,7 +566,7 @@ def main():
                                "1x128+128x1 quantization, fwd+dgrad+wgrad",
                    "tokens": 16384, "gemm_gflop_per_step": round(gemm_flops / 1e9, 1),
                    "parallelism": "single GPU"},
-        "roofline": roof, "cpu_baseline": cpu, "kernels": kernels, "mx_variant": mx_variant,
+        "roofline": roof, "cpu_baseline": cpu, "kernels": kernels, "configs": configs, "mx_variant": mx_variant,
     }
     print(json.dumps(out), flush=True)
     del keep
