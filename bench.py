@@ -126,15 +126,23 @@ def summarize_pmc(fetch_dir: str, write_dir: str):
         scale = COPY_BYTES / (copies[0] * 1024.0)
         # One op can be several dispatches: a split GEMM's reduce kernel runs right after the GEMM
         # kernel, and a GEMM whose leading rows run unsplit is two launches of the same GEMM kernel
-        # in a row (no GEMM op of the bench follows another of the same kernel).
-        last, prev = None, None
+        # in a row (no GEMM op of the bench follows another of the same kernel).  FWD and DGRAD both
+        # run the four-wave kernel and alternate in the step (X's FWD, then dY's DGRAD, per weight).
+        last, prev, w4_ops = None, None, 0
         for n, v in rows:
-            op = last if "split_reduce" in n else op_of_kernel(n)
-            cont = "split_reduce" in n or ("gemm_kernel" in n and n == prev)
+            gemm = "gemm_kernel" in n or "gemm_w4_kernel" in n
+            cont = "split_reduce" in n or (gemm and n == prev)
+            if "split_reduce" in n or cont:
+                op = last
+            elif "gemm_w4_kernel" in n:
+                op = "gemm_fwd" if w4_ops % 2 == 0 else "gemm_dgrad"
+                w4_ops += 1
+            else:
+                op = op_of_kernel(n)
             prev = n
             if op is None or op == "copy":
                 continue
-            if "gemm_kernel" in n:
+            if gemm:
                 last = op
             e = res.setdefault(op, {"FETCH_SIZE": 0.0, "WRITE_SIZE": 0.0, "launches": 0})
             e[counter] += v * 1024.0 * scale
