@@ -44,6 +44,8 @@ typedef float w4_v16f __attribute__((ext_vector_type(16)));
 constexpr int kW4Threads = 256;
 // 2 stages x (A 32 KB + B 32 KB), 2 stages x 2 KB of scales, 256 bytes that the L2 prefetches land in
 constexpr int kW4Lds = 131072 + 2 * 2048 + 256;
+// the bf16 epilogue stages 4 waves x 128 rows x 272 bytes, a little more than the K loop uses
+constexpr int kW4Smem = 4 * 128 * 272 > kW4Lds ? 4 * 128 * 272 : kW4Lds;
 constexpr uint32_t kRsrcWord3 = 0x00020000u; // raw buffer, 32-bit data format (gfx9 family)
 
 // Buffer resource of `bytes` bytes at `base` (stride 0: a plain byte range; reads past it return 0).
@@ -153,17 +155,19 @@ void gemm_w4_kernel(GemmArgs p) {
 #undef PURO_W4_INS
 #undef PURO_W4_CLOB
 
-  // ---- epilogue: each wave stages its quadrant in its own LDS region (bf16: all 128 rows, row stride
-  // 264 B; fp32: 64 rows at a time, 528 B; consecutive rows land 2 / 4 banks apart), then writes whole
-  // row segments with 16-byte stores, eight rows' reads in flight at a time.  The last slice block
-  // ended with a barrier, so LDS is free; the stores are not waited for (only the LDS reads).
+  // ---- epilogue: each wave stages its quadrant in its own LDS region (bf16: all 128 rows; fp32: 64
+  // rows at a time), then writes whole row segments with 16-byte stores, eight rows' reads in flight
+  // at a time.  Row strides of 272 / 528 bytes put consecutive rows 4 banks apart: the 32 lanes of a
+  // half-wave write 16 rows x 16 bytes (bf16) and hit 64 different banks, and the 16 lanes of a
+  // 16-byte read of one row do too.  The last slice block ended with a barrier, so LDS is free; the
+  // stores are not waited for (only the LDS reads).
   constexpr int kEs = OUT_BF16 ? 2 : 4;
-  constexpr int kRow = 128 * kEs + (OUT_BF16 ? 8 : 16);
+  constexpr int kRow = 128 * kEs + 16;
   constexpr int kStaged = OUT_BF16 ? 128 : 64;           // rows staged per pass
   constexpr int kLanesPerRow = 128 * kEs / 16;           // 16 (bf16) or 32 (fp32)
   constexpr int kRowsPerIt = 64 / kLanesPerRow;          // rows one 16-byte store instruction covers
   constexpr int kBatch = 8;
-  static_assert(4 * kStaged * kRow <= kW4Lds, "epilogue staging exceeds the LDS allocation");
+  static_assert(4 * kStaged * kRow <= kW4Smem, "epilogue staging exceeds the LDS allocation");
   uint8_t* wbuf = smem + wave * (kStaged * kRow);
   const bool cols_ok = n0 + 128 * wn < p.N;
   const int rr = lane / kLanesPerRow, rc = lane % kLanesPerRow;
@@ -249,15 +253,15 @@ hipError_t launch_w4(const GemmArgs& a, bool out_bf16, hipStream_t st) {
   const void* fn = out_bf16 ? reinterpret_cast<const void*>(&gemm_w4_kernel<true>)
                             : reinterpret_cast<const void*>(&gemm_w4_kernel<false>);
   if (!known || !attr_set[out_bf16][dev].load(std::memory_order_acquire)) {
-    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kW4Lds);
+    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kW4Smem);
     if (e != hipSuccess) return e;
     if (known) attr_set[out_bf16][dev].store(true, std::memory_order_release);
   }
   const dim3 grid((unsigned)(a.tiles_m * a.tiles_n * a.splits));
   if (out_bf16)
-    hipLaunchKernelGGL(gemm_w4_kernel<true>, grid, dim3(kW4Threads), kW4Lds, st, a);
+    hipLaunchKernelGGL(gemm_w4_kernel<true>, grid, dim3(kW4Threads), kW4Smem, st, a);
   else
-    hipLaunchKernelGGL(gemm_w4_kernel<false>, grid, dim3(kW4Threads), kW4Lds, st, a);
+    hipLaunchKernelGGL(gemm_w4_kernel<false>, grid, dim3(kW4Threads), kW4Smem, st, a);
   return hipGetLastError();
 }
 
