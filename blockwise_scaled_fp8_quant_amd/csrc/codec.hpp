@@ -84,7 +84,9 @@ __device__ __forceinline__ uint32_t cvt4(float a, float b, float c, float d) {
 // DPP helpers (row = 16 lanes).
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+  // every row and bank enabled and every control used here a permutation within a row: each lane
+  // receives a value, so no "old" operand (and no register zeroed for it) is needed
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
 }
 constexpr int kDppQuadXor1 = 0xB1;        // quad_perm [1,0,3,2]
 constexpr int kDppQuadXor2 = 0x4E;        // quad_perm [2,3,0,1]

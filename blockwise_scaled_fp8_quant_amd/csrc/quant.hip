@@ -207,28 +207,30 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(const uint16_t* __restr
 #pragma unroll
   for (int i = 0; i < 8; ++i) v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xp + i * ldx));
 
-  // token amax: rp[k] holds tokens 2k (low half) and 2k+1 (high half)
+  // One pass over the thread's values, each |x| pair folded into its token's and its column
+  // pair's maxima at once (so no |x| outlives its dword): rm[i] is token i's max over the
+  // thread's 8 columns, cm[d] the packed max of columns 8 tc + 2d (low) and 8 tc + 2d + 1 (high)
+  // over the thread's 8 tokens.
+  uint32_t rm[8], cm[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t a0 = abs2(v[i].x), a1 = abs2(v[i].y), a2 = abs2(v[i].z), a3 = abs2(v[i].w);
+    cm[0] = pk_max_u16(cm[0], a0);
+    cm[1] = pk_max_u16(cm[1], a1);
+    cm[2] = pk_max_u16(cm[2], a2);
+    cm[3] = pk_max_u16(cm[3], a3);
+    rm[i] = hmax16(pk_max_u16(pk_max_u16(a0, a1), pk_max_u16(a2, a3)));
+  }
+  // token amax over the tile's 128 columns: rp[k] holds tokens 2k (low half) and 2k+1 (high half)
   uint32_t rp[4];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    uint32_t m2[2];
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const u32x4 w = v[2 * k + e];
-      const uint32_t m = pk_max_u16(pk_max_u16(abs2(w.x), abs2(w.y)), pk_max_u16(abs2(w.z), abs2(w.w)));
-      m2[e] = hmax16(m);
-    }
-    rp[k] = row16_pkmax(m2[0] | (m2[1] << 16));
-  }
+  for (int k = 0; k < 4; ++k) rp[k] = row16_pkmax(rm[2 * k] | (rm[2 * k + 1] << 16));
   if (tc < 4) rowmax[tr * 4 + tc] = tc == 0 ? rp[0] : tc == 1 ? rp[1] : tc == 2 ? rp[2] : rp[3];
 
-  // column amax: cm[d] holds columns 8 tc + 2d (low) and 8 tc + 2d + 1 (high)
-  uint32_t cm[4];
+  // column amax over the tile's 128 tokens
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
-    uint32_t m = abs2(v[0][d]);
-#pragma unroll
-    for (int i = 1; i < 8; ++i) m = pk_max_u16(m, abs2(v[i][d]));
+    uint32_t m = cm[d];
     m = pk_max_u16(m, (uint32_t)__shfl_xor((int)m, 16));
     m = pk_max_u16(m, (uint32_t)__shfl_xor((int)m, 32));
     cm[d] = m;
@@ -470,28 +472,37 @@ __device__ __forceinline__ void quant_128x128_block(const uint16_t* __restrict__
     if (sT) sT[kb * NB + nb] = sc;
   }
 
+  // row p's codes: rc[p][0] = columns 0-3, rc[p][1] = columns 4-7 of the thread's 8 (byte c = column c)
   uint8_t* qp = q + n0 * ldq + k0;
+  uint32_t rc[8][2];
 #pragma unroll
   for (int p = 0; p < 8; ++p) {
     const u32x4 x = v[p];
-    u32x2 o;
-    o.x = cvt4(bf16_lo(x.x) * r, bf16_hi(x.x) * r, bf16_lo(x.y) * r, bf16_hi(x.y) * r);
-    o.y = cvt4(bf16_lo(x.z) * r, bf16_hi(x.z) * r, bf16_lo(x.w) * r, bf16_hi(x.w) * r);
+    rc[p][0] = cvt4(bf16_lo(x.x) * r, bf16_hi(x.x) * r, bf16_lo(x.y) * r, bf16_hi(x.y) * r);
+    rc[p][1] = cvt4(bf16_lo(x.z) * r, bf16_hi(x.z) * r, bf16_lo(x.w) * r, bf16_hi(x.w) * r);
+    const u32x2 o = {rc[p][0], rc[p][1]};
     __builtin_nontemporal_store(o, reinterpret_cast<u32x2*>(qp + p * ldq));
   }
   if (qT) {   // (uniform branch: qT is a kernel argument)
-    // column j of the thread's 8 columns: 8 rows -> two dwords of the staged [column][row quad] tile
+    // The block has one scale, so the transposed codes are the same bytes: each 4 x 4 byte square
+    // (rows 4u .. 4u+3, columns 4h .. 4h+3) is transposed with byte permutes (v_perm_b32 picks
+    // bytes 0-3 from its second operand and 4-7 from its first), giving column 4h + c's codes of
+    // rows 4u .. 4u+3 as one dword of the staged [column][row quad] tile.
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      float e[8];
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t x = v[i][j >> 1];
-        e[i] = ((j & 1) ? bf16_hi(x) : bf16_lo(x)) * r;
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t d0 = rc[4 * u][h], d1 = rc[4 * u + 1][h], d2 = rc[4 * u + 2][h], d3 = rc[4 * u + 3][h];
+        const uint32_t p01lo = __builtin_amdgcn_perm(d1, d0, 0x05010400u);   // d0.b0 d1.b0 d0.b1 d1.b1
+        const uint32_t p01hi = __builtin_amdgcn_perm(d1, d0, 0x07030602u);   // d0.b2 d1.b2 d0.b3 d1.b3
+        const uint32_t p23lo = __builtin_amdgcn_perm(d3, d2, 0x05010400u);
+        const uint32_t p23hi = __builtin_amdgcn_perm(d3, d2, 0x07030602u);
+        uint32_t* col = stage + (cc * 8 + 4 * h) * 33 + 2 * rg + u;
+        col[0] = __builtin_amdgcn_perm(p23lo, p01lo, 0x05040100u);           // byte 0 of d0 .. d3
+        col[33] = __builtin_amdgcn_perm(p23lo, p01lo, 0x07060302u);          // byte 1
+        col[66] = __builtin_amdgcn_perm(p23hi, p01hi, 0x05040100u);          // byte 2
+        col[99] = __builtin_amdgcn_perm(p23hi, p01hi, 0x07060302u);          // byte 3
       }
-      stage[(cc * 8 + j) * 33 + 2 * rg] = cvt4(e[0], e[1], e[2], e[3]);
-      stage[(cc * 8 + j) * 33 + 2 * rg + 1] = cvt4(e[4], e[5], e[6], e[7]);
-    }
     __syncthreads();
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
