@@ -408,6 +408,61 @@ def cpu_baseline(d, tokens: int):
             "seconds": dt}
 
 
+def smi_sampler(samples, stop):
+    """Poll amd-smi for socket power (W) and the mean GFX clock (MHz) until `stop` is set;
+    appends (time, watts, mhz) to `samples`."""
+    import re
+    import subprocess
+    smi = "/opt/rocm/bin/amd-smi"
+    while not stop.is_set():
+        try:
+            out = subprocess.run([smi, "metric", "-p", "-c"], capture_output=True, text=True, timeout=10).stdout
+        except (OSError, subprocess.TimeoutExpired):
+            return
+        t = time.time()
+        w = re.search(r"SOCKET_POWER: (\d+) W", out)
+        clks = [int(x) for x in re.findall(r"GFX_\d+:\s+CLK: (\d+) MHz", out)]
+        if w and clks:
+            samples.append((t, int(w.group(1)), sum(clks) / len(clks)))
+        stop.wait(0.05)
+
+
+def power_phases(ops, mxops, torch, secs):
+    """Board power and GFX clock while the step, the MX step and each of the step's op kinds run
+    back to back for `secs` seconds each (amd-smi samples; the first second of a phase is
+    skipped).  Prints one JSON line per phase: median socket power, median clock, achieved rate."""
+    import threading
+    samples, stop = [], threading.Event()
+    th = threading.Thread(target=smi_sampler, args=(samples, stop), daemon=True)
+    th.start()
+    phases = [("idle", [], 3.0), ("step", ops, secs), ("mx_step", mxops, secs)]
+    for kind in ("gemm_fwd", "gemm_dgrad", "gemm_wgrad", "quant_act_dual", "quant_w_128x128"):
+        phases.append((kind, [o for o in ops if o[0] == kind], secs))
+    for name, sel, dur in phases:
+        torch.cuda.synchronize()
+        t0, n = time.time(), 0
+        if not sel:
+            time.sleep(dur)
+        while sel and time.time() - t0 < dur:
+            for _ in range(10):
+                for o in sel:
+                    o[1]()
+            torch.cuda.synchronize()
+            n += 10
+        t1 = time.time()
+        got = [x for x in samples if t0 + 1.0 <= x[0] <= t1]
+        flops = sum(o[2].get("flops", 0.0) for o in sel) * n
+        nbytes = sum(o[2].get("bytes", 0.0) for o in sel if o[2].get("kind") == "quant") * n
+        print(json.dumps({
+            "phase": name, "seconds": round(t1 - t0, 2), "passes": n, "smi_samples": len(got),
+            "socket_power_w": statistics.median([x[1] for x in got]) if got else None,
+            "gfx_clock_mhz": round(statistics.median([x[2] for x in got])) if got else None,
+            "TFLOP/s": round(flops / (t1 - t0) / 1e12, 1) if flops else None,
+            "GB/s": round(nbytes / (t1 - t0) / 1e9, 1) if nbytes else None}), flush=True)
+    stop.set()
+    th.join(timeout=15)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -417,6 +472,8 @@ def main():
     ap.add_argument("--no-configs", action="store_true", help="skip the other named configurations")
     ap.add_argument("--cpu-tokens", type=int, default=2048)
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--power-phases", type=float, metavar="SECONDS",
+                    help="instead of timing: board power and clock per phase (needs amd-smi)")
     args = ap.parse_args()
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc)
@@ -437,6 +494,9 @@ def main():
     log(f"  drawn in {time.time() - t0:.1f} s")
     ops, single, mxops, keep = build_step(P, torch, d)
     stream = torch.cuda.current_stream()
+    if args.power_phases:
+        power_phases(ops, mxops, torch, args.power_phases)
+        return
 
     # calibration copy for the HBM-traffic counters (untimed; reads and writes COPY_BYTES)
     src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0")
