@@ -254,3 +254,42 @@ def test_w_outlier_isolation_and_extremes(P):
     x[0:128, 0:128] = 0.0
     x[256:384, 128:256] *= 1e-35
     check_w(P, bf16(x), "outlier/zero/tiny blocks")
+
+
+def test_w_transposed_codes_every_byte_value(P):
+    """Values spread so that a block's codes take (nearly) every E4M3 byte in every position of a
+    thread's 8 x 8 sub-block: the transposed copy must be the byte transpose of the row codes
+    (the kernel builds it from them with byte permutes) and equal the oracle's."""
+    rng = np.random.default_rng(31)
+    mags = 2.0 ** rng.uniform(-9.0, 8.8, (256, 512))
+    x = (np.where(rng.random((256, 512)) < 0.5, -1.0, 1.0) * mags).astype(np.float32)
+    x[0:128, 0:128] *= 1e-3                              # a second block scale
+    bits = bf16(x)
+    q, s, qT, sT = P.puro_fp8_quant_w_128x128(bf16_dev(bits), transposed=True)
+    q, qT = host(q), host(qT)
+    assert len(np.unique(q[128:256, 128:256])) > 200, "the probe should cover most code bytes"
+    assert_bytes_equal(qT, np.ascontiguousarray(q.T), "codes^T vs transpose of codes")
+    check_w(P, bits, "every byte value")
+
+
+def test_w_nonfinite_reading(P):
+    """A NaN in a block gives a NaN scale and NaN codes for the whole block; an inf gives scale +inf
+    and a NaN code at the inf (zero elsewhere).  The transposed copy holds the same bytes."""
+    x = np.ones((256, 384), np.float32) * 0.5
+    x[3, 5] = np.nan                                      # block (0, 0)
+    x[140, 300] = np.inf                                  # block (1, 2)
+    bits = bf16(x)
+    q, s, qT, sT = P.puro_fp8_quant_w_128x128(bf16_dev(bits), transposed=True)
+    q, s, qT, sT = host(q), host(s), host(qT), host(sT)
+    assert np.isnan(s[0, 0]) and e4m3.is_nan_code(q[:128, :128]).all()
+    assert s[1, 2] == np.inf and e4m3.is_nan_code(q[140, 300])
+    blk = q[128:256, 256:384].copy()
+    blk[12, 44] = 0
+    assert (blk == 0).all()
+    assert_bytes_equal(qT, np.ascontiguousarray(q.T), "codes^T vs transpose of codes")
+    assert_bytes_equal(sT, np.ascontiguousarray(s.T), "scales^T vs transpose of scales")
+    rq, rs, _, _ = quant.quant_w_128x128(bits)
+    for bi, bj in ((0, 1), (0, 2), (1, 0), (1, 1)):       # the finite blocks
+        assert_bytes_equal(q[128 * bi:128 * bi + 128, 128 * bj:128 * bj + 128],
+                           rq[128 * bi:128 * bi + 128, 128 * bj:128 * bj + 128], f"finite block {bi},{bj}")
+        assert_bytes_equal(s[bi, bj], rs[bi, bj], f"finite block scale {bi},{bj}")
