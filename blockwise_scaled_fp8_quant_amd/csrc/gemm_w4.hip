@@ -21,8 +21,8 @@
 //    buffer_load ... lds (no VGPR round trip).  The buffer resources span the tile's valid rows, so
 //    rows past M or N read as zero (half-filled edge tiles need no clamping).
 //  * Tiles are visited in the XCD-aware order of tile_of (gemm_args.hpp).
-//  * The epilogue stages each wave's quadrant through LDS, 64 rows at a time, and writes whole
-//    row segments with 16-byte stores.
+//  * The epilogue stages each wave's quadrant through LDS (bf16: all 128 rows at once; fp32: 64
+//    rows at a time) and writes whole row segments with 16-byte stores.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
