@@ -232,7 +232,7 @@ const char* puro_fp8_strerror(int status) {
     case PURO_ERR_DTYPE: return "unknown output dtype";
     case PURO_ERR_WORKSPACE: return "workspace too small";
     case PURO_ERR_HIP: return "HIP runtime error at launch";
-    case PURO_ERR_UNSUPPORTED: return "request outside what this build implements";
+    case PURO_ERR_UNSUPPORTED: return "request outside what this library implements";
     default: return "unknown status";
   }
 }

@@ -59,7 +59,7 @@ enum {
   PURO_ERR_DTYPE = -6,       /* unknown output dtype */
   PURO_ERR_WORKSPACE = -7,   /* workspace smaller than puro_fp8_gemm_workspace_size() */
   PURO_ERR_HIP = -8,         /* the HIP runtime reported an error at launch */
-  PURO_ERR_UNSUPPORTED = -9  /* valid request this build does not implement (e.g. a size limit) */
+  PURO_ERR_UNSUPPORTED = -9  /* valid request this library does not implement (e.g. a size limit) */
 };
 
 enum { PURO_GEMM_FWD = 0, PURO_GEMM_DGRAD = 1, PURO_GEMM_WGRAD = 2 };
