@@ -60,12 +60,14 @@ COPY_BYTES = 256 << 20          # calibration copy: 256 MiB read + 256 MiB writt
 
 
 def kernel_source_hash() -> str:
-    """Hash of the native sources' code: comments and blank space are left out, so that an edit of
-    a comment keeps the traffic counters taken on the same code."""
+    """Hash of the code of the kernels and their launch plans (the HIP sources and the headers and
+    generated sequences they include; the host-only C ABI layer is left out): comments and blank
+    space are ignored, so that an edit of a comment keeps the traffic counters taken on the same
+    code."""
     import re
     h = hashlib.sha256()
     for f in sorted(os.listdir(CSRC)):
-        if f.endswith((".hip", ".hpp", ".cpp", ".inc", ".h")):
+        if f.endswith((".hip", ".hpp", ".inc")):
             with open(os.path.join(CSRC, f), encoding="utf-8") as fh:
                 text = fh.read()
             text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
