@@ -525,6 +525,7 @@ static hipError_t launch_rows(int mode, int64_t M, int64_t N, int64_t K, int spl
   a.accumulate = accumulate ? 1 : 0;
   a.q = q; a.ldq = ldq; a.qs = qs; a.ldqs = ldqs;
   if (q != nullptr) {
+    if (kUseW4 && (mode == 0 || mode == 1) && w4_supported(a)) return launch_w4(a, true, st);
     switch (mode) {
       case 0: return launch_one<0, true, true>(a, st);
       case 1: return launch_one<1, true, true>(a, st);

@@ -21,12 +21,17 @@
 //    buffer_load ... lds (no VGPR round trip).  The buffer resources span the tile's valid rows, so
 //    rows past M or N read as zero (half-filled edge tiles need no clamping).
 //  * Tiles are visited in the XCD-aware order of tile_of (gemm_args.hpp).
-//  * The epilogue stages each wave's quadrant through LDS (bf16: all 128 rows at once; fp32: 64
-//    rows at a time) and writes whole row segments with 16-byte stores.
+//  * The epilogue stages each wave's quadrant through LDS (bf16: all 128 rows at once; fp32, and
+//    bf16 with the fused output quantization: 64 rows at a time) and writes whole row segments
+//    with 16-byte stores.
+//  * Optionally (QUANT, FWD / DGRAD with bf16 output) the epilogue also writes the 1x128
+//    quantization of C along N: a wave's 128 columns are one group, held by the 4 lanes that share
+//    a row, and the quantizer's numerics are applied to the bf16 values it writes.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
 
+#include "codec.hpp"
 #include "gemm_args.hpp"
 #include "gemm_w4_asm.inc"
 #include "internal.hpp"
@@ -62,9 +67,10 @@ __device__ __forceinline__ w4_v4i rsrc(const void* base, int64_t bytes) {
 
 }  // namespace
 
-template <bool OUT_BF16>
+template <bool OUT_BF16, bool QUANT>
 __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_w4_kernel(GemmArgs p) {
+  static_assert(!QUANT || OUT_BF16, "the fused output quantization needs the bf16 output");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
   const int t = threadIdx.x;
@@ -163,12 +169,17 @@ void gemm_w4_kernel(GemmArgs p) {
   // stores are not waited for (only the LDS reads).
   constexpr int kEs = OUT_BF16 ? 2 : 4;
   constexpr int kRow = 128 * kEs + 16;
-  constexpr int kStaged = OUT_BF16 ? 128 : 64;           // rows staged per pass
+  constexpr int kStaged = OUT_BF16 && !QUANT ? 128 : 64; // rows staged per pass
   constexpr int kLanesPerRow = 128 * kEs / 16;           // 16 (bf16) or 32 (fp32)
   constexpr int kRowsPerIt = 64 / kLanesPerRow;          // rows one 16-byte store instruction covers
   constexpr int kBatch = 8;
   static_assert(4 * kStaged * kRow <= kW4Smem, "epilogue staging exceeds the LDS allocation");
   uint8_t* wbuf = smem + wave * (kStaged * kRow);
+  // QUANT: the codes of the staged rows, 128 bytes per row at a 144-byte stride (a row of 36 dwords:
+  // the 16 rows x 4 lanes of one code write hit 64 different banks), behind the 4 waves' C staging
+  constexpr int kQRow = 144;
+  static_assert(!QUANT || 4 * kStaged * (kRow + kQRow) <= kW4Smem, "code staging exceeds the LDS allocation");
+  uint8_t* qbuf = smem + 4 * kStaged * kRow + wave * (kStaged * kQRow);
   const bool cols_ok = n0 + 128 * wn < p.N;
   const int rr = lane / kLanesPerRow, rc = lane % kLanesPerRow;
 #pragma unroll
@@ -199,6 +210,40 @@ void gemm_w4_kernel(GemmArgs p) {
           *reinterpret_cast<g_f32x4*>(dst) = o;
         }
       }
+      if constexpr (QUANT) {
+        // the row's 1x128 group: this lane's 32 bf16 values (columns 16 ni + 4 g .. +3), then the
+        // other three lanes of the row (lanes l16 + 16 g); the same numerics as quant_1x128_kernel
+        uint32_t am2 = 0;
+        g_u32x2 o[8];
+#pragma unroll
+        for (int ni = 0; ni < 8; ++ni) {
+          float v[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            if (ni < 7) {
+              const int tt = 7 * mi + ni;
+              v[r] = acc[tt >> 2][4 * (tt & 3) + r];
+            } else {
+              v[r] = agp[mi][r];
+            }
+          }
+          o[ni][0] = bf16x2_rne(v[0], v[1]);
+          o[ni][1] = bf16x2_rne(v[2], v[3]);
+          am2 = pk_max_u16(am2, pk_max_u16(abs2(o[ni][0]), abs2(o[ni][1])));
+        }
+        uint32_t am = hmax16(am2);
+        am = umax(am, (uint32_t)__shfl_xor((int)am, 16));
+        am = umax(am, (uint32_t)__shfl_xor((int)am, 32));
+        float sc, r;
+        tile_scale(am, sc, r);
+        const int srow = 16 * (mi - kGroups * h) + l16;           // row within the staged rows
+#pragma unroll
+        for (int ni = 0; ni < 8; ++ni)
+          *reinterpret_cast<uint32_t*>(qbuf + srow * kQRow + 16 * ni + 4 * g) =
+              cvt4(bf16_lo(o[ni][0]) * r, bf16_hi(o[ni][0]) * r, bf16_lo(o[ni][1]) * r, bf16_hi(o[ni][1]) * r);
+        const int row = m0 + 128 * wm + 16 * mi + l16;
+        if (g == 0 && row < p.M && cols_ok) p.qs[(int64_t)((n0 >> 7) + wn) * p.ldqs + row] = sc;
+      }
     }
     // the wave reads back its own rows: wait for its LDS writes only
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -225,6 +270,16 @@ void gemm_w4_kernel(GemmArgs p) {
           *cp = o;
         }
       }
+      if constexpr (QUANT) {
+        // the staged codes: 8 lanes x 16 bytes per 128-byte row, 8 rows per store instruction
+        uint8_t* qrow = p.q + (int64_t)row0 * p.ldq + n0 + 128 * wn;
+#pragma unroll
+        for (int it = 0; it < kStaged / 8; ++it) {
+          const int r = 8 * it + (lane >> 3), part = lane & 7;
+          *reinterpret_cast<g_u32x4*>(qrow + (int64_t)r * p.ldq + part * 16) =
+              *reinterpret_cast<const g_u32x4*>(qbuf + r * kQRow + part * 16);
+        }
+      }
     }
     if (h + 1 < 128 / kStaged) {
       // the next pass overwrites the staging area: this pass's reads must have returned
@@ -244,24 +299,30 @@ bool w4_supported(const GemmArgs& a) {
 }
 
 hipError_t launch_w4(const GemmArgs& a, bool out_bf16, hipStream_t st) {
+  // variant: 0 fp32 out, 1 bf16 out, 2 bf16 out with the fused 1x128 quantization (a.q set)
+  const int variant = a.q != nullptr ? 2 : (out_bf16 ? 1 : 0);
+  if (variant == 2 && !out_bf16) return hipErrorInvalidValue;
   constexpr int kMaxDevices = 64;
-  static std::atomic<bool> attr_set[2][kMaxDevices];
+  static std::atomic<bool> attr_set[3][kMaxDevices];
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   const bool known = dev >= 0 && dev < kMaxDevices;
-  const void* fn = out_bf16 ? reinterpret_cast<const void*>(&gemm_w4_kernel<true>)
-                            : reinterpret_cast<const void*>(&gemm_w4_kernel<false>);
-  if (!known || !attr_set[out_bf16][dev].load(std::memory_order_acquire)) {
+  const void* fn = variant == 2 ? reinterpret_cast<const void*>(&gemm_w4_kernel<true, true>)
+                 : variant == 1 ? reinterpret_cast<const void*>(&gemm_w4_kernel<true, false>)
+                                : reinterpret_cast<const void*>(&gemm_w4_kernel<false, false>);
+  if (!known || !attr_set[variant][dev].load(std::memory_order_acquire)) {
     e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kW4Smem);
     if (e != hipSuccess) return e;
-    if (known) attr_set[out_bf16][dev].store(true, std::memory_order_release);
+    if (known) attr_set[variant][dev].store(true, std::memory_order_release);
   }
   const dim3 grid((unsigned)(a.tiles_m * a.tiles_n * a.splits));
-  if (out_bf16)
-    hipLaunchKernelGGL(gemm_w4_kernel<true>, grid, dim3(kW4Threads), kW4Smem, st, a);
+  if (variant == 2)
+    hipLaunchKernelGGL((gemm_w4_kernel<true, true>), grid, dim3(kW4Threads), kW4Smem, st, a);
+  else if (variant == 1)
+    hipLaunchKernelGGL((gemm_w4_kernel<true, false>), grid, dim3(kW4Threads), kW4Smem, st, a);
   else
-    hipLaunchKernelGGL(gemm_w4_kernel<false>, grid, dim3(kW4Threads), kW4Smem, st, a);
+    hipLaunchKernelGGL((gemm_w4_kernel<false, false>), grid, dim3(kW4Threads), kW4Smem, st, a);
   return hipGetLastError();
 }
 
