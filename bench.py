@@ -83,7 +83,7 @@ def op_of_kernel(name: str):
         return "mx_quant_dual"
     if "gemm_kernel<3" in name:
         return "mx_gemm"
-    if "gemm_kernel<0, true, true>" in name:
+    if "gemm_kernel<0, true, true>" in name or "gemm_w4_kernel<true, true>" in name:
         return "gemm_fwd_quant_out"
     if "gemm_kernel<0" in name:
         return "gemm_fwd"
@@ -135,14 +135,15 @@ def summarize_pmc(fetch_dir: str, write_dir: str):
         # One op can be several dispatches: a split GEMM's reduce kernel runs right after the GEMM
         # kernel, and a GEMM whose leading rows run unsplit is two launches of the same GEMM kernel
         # in a row (no GEMM op of the bench follows another of the same kernel).  FWD and DGRAD both
-        # run the four-wave kernel and alternate in the step (X's FWD, then dY's DGRAD, per weight).
+        # run the four-wave kernel and alternate in the step (X's FWD, then dY's DGRAD, per weight);
+        # its fused-quantization instance is the standalone FWD with the output quantized.
         last, prev, w4_ops = None, None, 0
         for n, v in rows:
             gemm = "gemm_kernel" in n or "gemm_w4_kernel" in n
             cont = "split_reduce" in n or (gemm and n == prev)
             if "split_reduce" in n or cont:
                 op = last
-            elif "gemm_w4_kernel" in n:
+            elif "gemm_w4_kernel" in n and op_of_kernel(n) is None:
                 op = "gemm_fwd" if w4_ops % 2 == 0 else "gemm_dgrad"
                 w4_ops += 1
             else:
