@@ -81,7 +81,7 @@ def op_of_kernel(name: str):
     """Map a dispatched kernel's name to the bench op it belongs to (None: not a path kernel)."""
     if "mx_quant_dual" in name:
         return "mx_quant_dual"
-    if "gemm_kernel<3" in name:
+    if "gemm_kernel<3" in name or "gemm_w4mx_kernel" in name:
         return "mx_gemm"
     if "gemm_kernel<0, true, true>" in name or "gemm_w4_kernel<true, true>" in name:
         return "gemm_fwd_quant_out"
@@ -139,7 +139,7 @@ def summarize_pmc(fetch_dir: str, write_dir: str):
         # its fused-quantization instance is the standalone FWD with the output quantized.
         last, prev, w4_ops = None, None, 0
         for n, v in rows:
-            gemm = "gemm_kernel" in n or "gemm_w4_kernel" in n
+            gemm = "gemm_kernel" in n or "gemm_w4_kernel" in n or "gemm_w4mx_kernel" in n
             cont = "split_reduce" in n or (gemm and n == prev)
             if "split_reduce" in n or cont:
                 op = last

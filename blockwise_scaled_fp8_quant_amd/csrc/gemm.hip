@@ -502,7 +502,7 @@ static hipError_t launch_rows(int mode, int64_t M, int64_t N, int64_t K, int spl
       case 0: e = w4 ? launch_w4(a, false, st) : launch_one<0, false>(a, st); break;
       case 1: e = w4 ? launch_w4(a, false, st) : launch_one<1, false>(a, st); break;
       case 2: e = launch_one<2, false>(a, st); break;
-      default: e = launch_one<kModeMx, false>(a, st); break;
+      default: e = kUseW4 && w4mx_supported(a) ? launch_w4mx(a, false, st) : launch_one<kModeMx, false>(a, st); break;
     }
     if (e != hipSuccess) return e;
     const int64_t work = M * (N / 4);
@@ -534,6 +534,7 @@ static hipError_t launch_rows(int mode, int64_t M, int64_t N, int64_t K, int spl
     }
   }
   if (kUseW4 && (mode == 0 || mode == 1) && w4_supported(a)) return launch_w4(a, out_bf16, st);
+  if (kUseW4 && mode == kModeMx && !accumulate && w4mx_supported(a)) return launch_w4mx(a, out_bf16, st);
   switch (mode * 2 + (out_bf16 ? 1 : 0)) {
     case 0: return launch_one<0, false>(a, st);
     case 1: return launch_one<0, true>(a, st);

@@ -65,5 +65,8 @@ __device__ __forceinline__ void tile_of(int b, int tiles_m, int tiles_n, int gro
 hipError_t launch_w4(const GemmArgs& a, bool out_bf16, hipStream_t st);
 // Whether launch_w4 can take these arguments: its operand offsets are 32-bit buffer offsets.
 bool w4_supported(const GemmArgs& a);
+// The MXFP8 GEMM in the four-wave form (E8M0 block scales in sA / sB), and its offset check.
+hipError_t launch_w4mx(const GemmArgs& a, bool out_bf16, hipStream_t st);
+bool w4mx_supported(const GemmArgs& a);
 
 }  // namespace puro
