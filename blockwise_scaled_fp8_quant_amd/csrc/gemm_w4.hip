@@ -238,10 +238,12 @@ void gemm_w4_kernel(GemmArgs p) {
   const int sstep = __builtin_amdgcn_readfirstlane((int)(p.ldsa * 4));
   const int mw = wave * 8192, ms = 131072 + 256 * wave;
 
-  // ---- fragment read addresses (stage 0): the lane's two 16-byte chunks of its row; every row a
-  // lane reads has the swizzle term (lane & 15) >> 1 (row offsets are multiples of 16)
+  // ---- fragment read addresses (stage 0): the lane's two 16-byte chunks of its row, g and g + 4 (any
+  // assignment that A and B share gives the same slice sum; this one, the MXFP8 kernel's, keeps the
+  // reads off each other's banks); every row a lane reads has the swizzle term (lane & 15) >> 1 (row
+  // offsets are multiples of 16)
   const int l16 = lane & 15, g = lane >> 4, sw = l16 >> 1;
-  const uint32_t c0 = (uint32_t)(((2 * g) ^ sw) << 4), c1 = (uint32_t)(((2 * g + 1) ^ sw) << 4);
+  const uint32_t c0 = (uint32_t)((g ^ sw) << 4), c1 = (uint32_t)(((g + 4) ^ sw) << 4);
   const uint32_t aj0 = (uint32_t)((128 * wm + l16) * 128) + c0, aj1 = (uint32_t)((128 * wm + l16) * 128) + c1;
   const uint32_t bj0 = 65536u + (uint32_t)((128 * wn + l16) * 128) + c0;
   const uint32_t bj1 = 65536u + (uint32_t)((128 * wn + l16) * 128) + c1;
