@@ -100,9 +100,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
   const int wm = wave >> 1, wn = wave & 1;
   const int l32 = lane & 31, h = lane >> 5;
   int tm, tn;
-  const int ntiles = p.tiles_m * p.tiles_n;
-  const int split = blockIdx.x / ntiles;
-  tile_of(blockIdx.x - split * ntiles, p.tiles_m, p.tiles_n, p.group, tm, tn);
+  int split;
+  block_of(blockIdx.x, p.tiles_m, p.tiles_n, p.splits, p.group, split, tm, tn);
   const int m0 = tm * kBM, n0 = tn * kBN;
   const int nk = p.K / kBK;                       // slices of the whole contraction
   const int kb_begin = split * p.kb_per_split;    // this block's slice range
@@ -461,14 +460,22 @@ static hipError_t launch_one(const GemmArgs& a, hipStream_t st) {
 #endif
 constexpr bool kUseW4 = PURO_GEMM_W4 != 0;
 
-// Tile rows per group (see tile_of).  The A rows of a group take group x 256 x K bytes of
+// Tile rows per group (see block_of).  The A rows of a group take group x 256 x K bytes of
 // the XCD's 4 MB L2.  Up to K = 2048, 4 rows (2 MB) stay resident from one wave of tiles to
-// the next while the B columns stream past, and 8 rows (4 MB) would not; beyond that no
-// group's rows survive a wave and 8 rows share each B slice between more workgroups.
-// (Measured on MI355X at 16384 tokens: 16384 x 12288 x 2048 FWD gains 13% with 4 rows.)
-static int choose_group(int64_t M, int64_t N, int64_t K) {
-  (void)M; (void)N;
-  return K <= 2048 ? 4 : 8;
+// the next while the B columns stream past, and 8 rows (4 MB) would not (measured on MI355X at
+// 16384 tokens: 16384 x 12288 x 2048 FWD gains 13% with 4 rows).  Beyond that no group's rows
+// survive a wave, and what counts is how many operand panels (tile rows plus tile columns) the
+// up to 32 workgroups an XCD runs at once touch: 8 rows, unless 4 touch fewer (a 192-workgroup
+// grid's 24 per XCD: 4 rows x 6 columns against 8 x 3).
+static int choose_group(int64_t M, int64_t N, int64_t K, int splits) {
+  if (K <= 2048) return 4;
+  const int64_t tm = (M + kBM - 1) / kBM, tn = (N + kBN - 1) / kBN;
+  const int64_t run = std::max<int64_t>(1, std::min<int64_t>(32, tm * tn * splits / 8));
+  auto panels = [&](int64_t g) {
+    const int64_t rows = std::min(g, tm);
+    return rows + std::min(tn, (run + rows - 1) / rows);
+  };
+  return panels(4) < panels(8) ? 4 : 8;
 }
 
 // One GEMM launch (and its split-K reduce) over M rows of A and C; the slices of sA are ldsa
@@ -487,7 +494,7 @@ static hipError_t launch_rows(int mode, int64_t M, int64_t N, int64_t K, int spl
   a.accumulate = 0;
   a.q = nullptr; a.ldq = 0; a.qs = nullptr; a.ldqs = 0;
   a.splits = splits;
-  a.group = choose_group(M, N, K);
+  a.group = choose_group(M, N, K, splits);
   a.kb_per_split = (int)((K / kBK + a.splits - 1) / a.splits);
   a.split_stride = 0;
   if (a.splits > 1) {

@@ -22,7 +22,7 @@ __device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
 struct GemmArgs {
   int M, N, K;
   int tiles_m, tiles_n;
-  int group;             // tile rows walked together (see tile_of)
+  int group;             // tile rows walked together (see block_of)
   int splits;            // contraction split: block b works on split b / (tiles_m * tiles_n)
   int kb_per_split;      // 128-deep slices per split
   int64_t split_stride;  // elements between the fp32 partial outputs of consecutive splits
@@ -43,21 +43,26 @@ struct GemmArgs {
   int64_t ldqs;
 };
 
-// Map the linear workgroup id to a (tile_m, tile_n) pair: XCD-contiguous, grouped rows.  The
-// dispatcher places workgroup b on XCD b % 8; each XCD gets a contiguous run of the tile
-// sequence, which walks `group` tile rows at a time across all tile columns, so the A rows of
-// a group stay in that XCD's L2 while the B columns stream past (B is read by every XCD and
-// is shared through the memory-side cache).
-__device__ __forceinline__ void tile_of(int b, int tiles_m, int tiles_n, int group, int& tm, int& tn) {
+// Map the linear workgroup id to (split, tile_m, tile_n).  The dispatcher places workgroup b on XCD
+// b % 8; each XCD gets a contiguous run of the split-major tile sequence, so with a contraction
+// split the workgroups of one XCD share their split's slice range rather than each running a
+// piece of every split.  Within a split the sequence walks `group` tile rows at a time across all
+// tile columns: an XCD's run is then a compact block of tiles whose A rows and B columns its
+// workgroups read from the XCD's L2 (B is also shared between XCDs through the memory-side cache).
+__host__ __device__ inline void block_of(int b, int tiles_m, int tiles_n, int splits, int group, int& split,
+                                         int& tm, int& tn) {
   const int nt = tiles_m * tiles_n;
-  const int full = (nt >> 3) << 3;
+  const int total = nt * splits;
+  const int full = (total >> 3) << 3;
   int logical = b;
-  if (b < full) logical = (b & 7) * (nt >> 3) + (b >> 3);
+  if (b < full) logical = (b & 7) * (total >> 3) + (b >> 3);
+  split = logical / nt;
+  const int t = logical - split * nt;
   const int per_group = group * tiles_n;
-  const int g = logical / per_group;
+  const int g = t / per_group;
   const int first_m = g * group;
-  const int gsize = min(tiles_m - first_m, group);
-  const int r = logical - g * per_group;
+  const int gsize = tiles_m - first_m < group ? tiles_m - first_m : group;
+  const int r = t - g * per_group;
   tm = first_m + r % gsize;
   tn = r / gsize;
 }

@@ -20,7 +20,7 @@
 //    slice's A and B rows (256 x 128 bytes each) and scales are copied into the other with
 //    buffer_load ... lds (no VGPR round trip).  The buffer resources span the tile's valid rows, so
 //    rows past M or N read as zero (half-filled edge tiles need no clamping).
-//  * Tiles are visited in the XCD-aware order of tile_of (gemm_args.hpp).
+//  * Tiles are visited in the XCD-aware order of block_of (gemm_args.hpp).
 //  * The epilogue stages each wave's quadrant through LDS (bf16: all 128 rows at once; fp32, and
 //    bf16 with the fused output quantization: 64 rows at a time) and writes whole row segments
 //    with 16-byte stores.
@@ -200,9 +200,8 @@ void gemm_w4_kernel(GemmArgs p) {
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   int tm, tn;
-  const int ntiles = p.tiles_m * p.tiles_n;
-  const int split = blockIdx.x / ntiles;
-  tile_of(blockIdx.x - split * ntiles, p.tiles_m, p.tiles_n, p.group, tm, tn);
+  int split;
+  block_of(blockIdx.x, p.tiles_m, p.tiles_n, p.splits, p.group, split, tm, tn);
   const int m0 = tm * 256, n0 = tn * 256;
   const int nk = p.K / 128;
   const int kb_begin = split * p.kb_per_split;
@@ -302,9 +301,8 @@ void gemm_w4mx_kernel(GemmArgs p) {
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   int tm, tn;
-  const int ntiles = p.tiles_m * p.tiles_n;
-  const int split = blockIdx.x / ntiles;
-  tile_of(blockIdx.x - split * ntiles, p.tiles_m, p.tiles_n, p.group, tm, tn);
+  int split;
+  block_of(blockIdx.x, p.tiles_m, p.tiles_n, p.splits, p.group, split, tm, tn);
   const int m0 = tm * 256, n0 = tn * 256;
   const int nk = p.K / 128;
   const int kb_begin = split * p.kb_per_split;
