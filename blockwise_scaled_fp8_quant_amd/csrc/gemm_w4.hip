@@ -68,6 +68,22 @@ __device__ __forceinline__ w4_v4i rsrc(const void* base, int64_t bytes) {
 
 }  // namespace
 
+// ---- which rows a wave's L2 prefetch touches.  The workgroups an XCD runs at once form a block of
+// `group` tile rows by 32 / group tile columns (block_of), and each line only has to reach that
+// XCD's L2 once: an A row panel is shared by the block's tiles of one tile row (n_a of them, told
+// apart by tile column mod n_a), a B panel by its tiles of one tile column (n_b, by tile row mod
+// n_b).  So of each run of n lanes (n = n_a or n_b) only one row is fetched, the one whose class
+// is the tile's: the lanes of the run all point at it and their requests merge into one line.
+__device__ __forceinline__ int pf_share_a(const GemmArgs& p) {
+  const int n = min(32 / p.group, p.tiles_n);
+  return n >= 8 ? 8 : n >= 4 ? 4 : n >= 2 ? 2 : 1;
+}
+__device__ __forceinline__ int pf_share_b(const GemmArgs& p) {
+  const int n = min(p.group, p.tiles_m);
+  return n >= 8 ? 8 : n >= 4 ? 4 : n >= 2 ? 2 : 1;
+}
+__device__ __forceinline__ int pf_row(int lane, int tile, int n) { return (lane & ~(n - 1)) + (tile & (n - 1)); }
+
 // ---- epilogue of both four-wave kernels: `val(mi, ni, r)` is element r (row 16 mi + lane % 16,
 // column 16 ni + 4 (lane / 16) + r of the wave's quadrant) of the finished accumulator.
 template <bool OUT_BF16, bool QUANT, typename Val>
@@ -229,8 +245,8 @@ void gemm_w4_kernel(GemmArgs p) {
   const uint32_t osa = (uint32_t)lane * 4u;
   // prefetch offsets: row 64 wave + lane (the wave's base row is in qa[0] / qb[0]), two slices ahead
   // of the one being copied; the prologue prefetches the second slice
-  uint32_t pfa = (uint32_t)(lane * p.lda) + k0 + 128u;
-  uint32_t pfb = (uint32_t)(lane * p.ldb) + k0 + 128u;
+  uint32_t pfa = (uint32_t)(pf_row(lane, tn, pf_share_a(p)) * p.lda) + k0 + 128u;
+  uint32_t pfb = (uint32_t)(pf_row(lane, tm, pf_share_b(p)) * p.ldb) + k0 + 128u;
   int ssp;                                         // row-scale offset of the prefetched slice
   int ssa = __builtin_amdgcn_readfirstlane((int)(((int64_t)kb_begin * p.ldsa + 64 * wave) * 4));
   int ssw = __builtin_amdgcn_readfirstlane((wn * nk + kb_begin) * 4);
@@ -327,8 +343,8 @@ void gemm_w4mx_kernel(GemmArgs p) {
   uint32_t ob0 = (uint32_t)(crow * p.ldb) + (uint32_t)((pch ^ (crow >> 1)) << 4) + k0;
   uint32_t ob1 = (uint32_t)(crow * p.ldb) + (uint32_t)((pch ^ (crow >> 1) ^ 4) << 4) + k0;
   const uint32_t osa = (uint32_t)lane * 4u;
-  uint32_t pfa = (uint32_t)(lane * p.lda) + k0 + 128u;
-  uint32_t pfb = (uint32_t)(lane * p.ldb) + k0 + 128u;
+  uint32_t pfa = (uint32_t)(pf_row(lane, tn, pf_share_a(p)) * p.lda) + k0 + 128u;
+  uint32_t pfb = (uint32_t)(pf_row(lane, tm, pf_share_b(p)) * p.ldb) + k0 + 128u;
   int ssp, ssq;                                    // scale offsets of the prefetched slice
   int ssa = __builtin_amdgcn_readfirstlane((int)(((int64_t)kb_begin * p.ldsa + 64 * wave) * 4));
   int ssb = __builtin_amdgcn_readfirstlane((int)(((int64_t)kb_begin * p.N + 64 * wave) * 4));
