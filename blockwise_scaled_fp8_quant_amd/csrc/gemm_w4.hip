@@ -68,21 +68,6 @@ __device__ __forceinline__ w4_v4i rsrc(const void* base, int64_t bytes) {
 
 }  // namespace
 
-// ---- which rows a wave's L2 prefetch touches.  The workgroups an XCD runs at once form a block of
-// `group` tile rows by 32 / group tile columns (block_of), and each line only has to reach that
-// XCD's L2 once: an A row panel is shared by the block's tiles of one tile row (n_a of them, told
-// apart by tile column mod n_a), a B panel by its tiles of one tile column (n_b, by tile row mod
-// n_b).  So of each run of n lanes (n = n_a or n_b) only one row is fetched, the one whose class
-// is the tile's: the lanes of the run all point at it and their requests merge into one line.
-__device__ __forceinline__ int pf_share_a(const GemmArgs& p) {
-  const int n = min(32 / p.group, p.tiles_n);
-  return n >= 8 ? 8 : n >= 4 ? 4 : n >= 2 ? 2 : 1;
-}
-__device__ __forceinline__ int pf_share_b(const GemmArgs& p) {
-  const int n = min(p.group, p.tiles_m);
-  return n >= 8 ? 8 : n >= 4 ? 4 : n >= 2 ? 2 : 1;
-}
-__device__ __forceinline__ int pf_row(int lane, int tile, int n) { return (lane & ~(n - 1)) + (tile & (n - 1)); }
 
 // ---- epilogue of both four-wave kernels: `val(mi, ni, r)` is element r (row 16 mi + lane % 16,
 // column 16 ni + 4 (lane / 16) + r of the wave's quadrant) of the finished accumulator.
