@@ -55,7 +55,6 @@ constexpr int kThreads = 512;
 constexpr int kStageA = kBM * kBK;              // 32 KB
 constexpr int kStageB = kBN * kBK;              // 32 KB
 constexpr int kStageBytes = kStageA + kStageB + 1024 + 1024;   // + sA tile + sB tile (fp32 x 256)
-constexpr int kPfBytes = 256;                  // WGRAD: where the L2 prefetches land (never read)
 
 // D = X * Y + Cin for X: 32x64 (lanes index rows), Y: 64x32 (lanes index columns), E4M3.
 // Zero scale operands select the unscaled instruction.
@@ -198,22 +197,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
   v16f pcarry = zero, sbcarry = zero;
   float scp = 0.0f;
 
-  // WGRAD: L2 prefetch of the slice after next, one dword per row: lanes 0-31 rows 32 wave + (lane & 31)
-  // of A, lanes 32-63 the same rows of B; of each run of lanes that share a panel with other
-  // resident tiles only one row is fetched (pf_row), rows clamped into the matrices
-  const uint8_t* pf_base = nullptr;
-  if constexpr (MODE == 2) {
-    const int pl = lane & 31;
-    pf_base = lane < 32
-        ? p.A + (int64_t)min(m0 + wave * 32 + pf_row(pl, tn, pf_share_a(p)), p.M - 1) * p.lda
-        : p.B + (int64_t)min(n0 + wave * 32 + pf_row(pl, tm, pf_share_b(p)), p.N - 1) * p.ldb;
-  }
-  uint8_t* const pf_lds = smem + 2 * kStageBytes;
-
   issue_slice(kb_begin, 0);
-  if constexpr (MODE == 2) {
-    if (kb_begin + 1 < kb_end) g2lds4(pf_base + (int64_t)(kb_begin + 1) * kBK, pf_lds);
-  }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
@@ -276,8 +260,6 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
     } else {
       // the lane's column scales: columns wn*128 + ni*32 + 8g + 4h .. +3 (ni, g immediates)
       const uint32_t sbj = sbase + (uint32_t)(kStageA + kStageB + 1024 + (wn * 128 + 4 * h) * 4);
-      // the prefetched slice: two ahead, within this block's range (the last ones repeat its end)
-      const uint8_t* pf = pf_base + (int64_t)min(kb + 2, kb_end - 1) * kBK;
       asm volatile(PURO_SLICE_ASM_COLSCALE
                    : "+{v[0:15]}"(acc[0]), "+{v[16:31]}"(acc[1]), "+{v[32:47]}"(acc[2]), "+{v[48:63]}"(acc[3]),
                      "+{v[64:79]}"(acc[4]), "+{v[80:95]}"(acc[5]), "+{v[96:111]}"(acc[6]), "+{v[112:127]}"(acc[7]),
@@ -289,8 +271,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
                      [ga0] "s"(a_grp[0] + ko), [ga1] "s"(a_grp[1] + ko), [ga2] "s"(a_grp[2] + ko),
                      [ga3] "s"(a_grp[3] + ko), [gb0] "s"(b_grp[0] + ko), [gb1] "s"(b_grp[1] + ko),
                      [gb2] "s"(b_grp[2] + ko), [gb3] "s"(b_grp[3] + ko), [oa0] "v"(a_off[0]), [oa1] "v"(a_off[1]),
-                     [ob0] "v"(b_off[0]), [ob1] "v"(b_off[1]), [m0] "s"(m0), [pf] "v"(pf),
-                     [pfl] "s"(lds_addr(pf_lds))
+                     [ob0] "v"(b_off[0]), [ob1] "v"(b_off[1]), [m0] "s"(m0)
                    : PURO_SLICE_ASM_COLSCALE_CLOBBERS, "m0", "scc", "memory");
     }
     scp = sc1;  // tile 7's product stays in pcarry until the next block (or the tail)
@@ -453,7 +434,7 @@ static int choose_splits(int64_t M, int64_t N, int64_t K) {
 
 template <int MODE, bool BF16, bool QUANT = false>
 static hipError_t launch_one(const GemmArgs& a, hipStream_t st) {
-  const int smem = 2 * kStageBytes + (MODE == 2 ? kPfBytes : 0);
+  const int smem = 2 * kStageBytes;
   // The dynamic-LDS limit is a per-device attribute of the kernel: set it once per device the
   // caller launches on (threads that race here all set the same value).
   constexpr int kMaxDevices = 64;

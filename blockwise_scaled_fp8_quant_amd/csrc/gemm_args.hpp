@@ -67,7 +67,7 @@ __host__ __device__ inline void block_of(int b, int tiles_m, int tiles_n, int sp
   tn = r / gsize;
 }
 
-// Which rows a wave's L2 prefetch of a later slice touches (both GEMM kernels).  The workgroups an
+// Which rows a wave's L2 prefetch of a later slice touches (four-wave kernels).  The workgroups an
 // XCD runs at once form a block of `group` tile rows by 32 / group tile columns (block_of), and each line only has to reach that
 // XCD's L2 once: an A row panel is shared by the block's tiles of one tile row (n_a of them, told
 // apart by tile column mod n_a), a B panel by its tiles of one tile column (n_b, by tile row mod

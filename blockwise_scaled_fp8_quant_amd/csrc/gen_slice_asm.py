@@ -73,7 +73,6 @@ HAZARD_WAIT_STATES = 20
 # still never holds more than two of them per wave.  Measured on MI355X against one copy per step:
 # FWD / DGRAD 4-7% faster, WGRAD 1-4%; all eight at once is slower than two per step.
 DMA_PLAN = [[0, 1], [2, 3], [4, 5], [6, 7], [], [], [], []]
-PF_STEP = 3                          # WGRAD: the L2 prefetch of the slice after next, after the copies
 STAGE_B = 32768                      # byte offset of the B tile in an LDS stage
 P_EVEN, P_ODD = 128, 144
 A0, A1, BF0, SB = 160, 176, 192, 208
@@ -160,14 +159,6 @@ class Emitter:
             self.emit("s_nop 0")
             self.emit(f"global_load_lds_dwordx4 %[ob{q & 1}], %[gb{q}]")
 
-    def prefetch(self):
-        """WGRAD: one dword of a row of the slice after next into an LDS area nothing reads (lanes
-        0-31 an A row, 32-63 a B row: %[pf] holds each lane's 64-bit address), so that its lines are
-        in L2 when the next block copies them."""
-        self.emit("s_mov_b32 m0, %[pfl]")
-        self.emit("s_nop 0")
-        self.emit("global_load_lds_dword %[pf], off")
-
     def fma_row(self, T, p, sc):
         for v in range(16):
             self.emit(f"v_fmac_f32 v{16 * T + v}, v{p + v}, %[{sc}]")
@@ -231,8 +222,6 @@ def gen_colscale():
         e.mfma_pair(P_EVEN if mi == 0 else P_ODD, BF0, A0 + 16 * mi)
         for k in DMA_PLAN[s]:
             e.dma(k)
-        if s == PF_STEP:
-            e.prefetch()
         if mi == 1 and ni < 3:
             e.frag(BF0, "bj", (ni + 1) * 4096)   # B(ni+1): the MFMAs reading B(ni) have issued
         if s == 0:
@@ -246,9 +235,7 @@ def gen_colscale():
             e.fma_col(2 * (q >> 1) + (q & 1), pq, f"sa{q & 1}")
             if mi == 0:                   # tile (ni-1, 1) was the last user of the old scales
                 e.sb_reads(ni)
-    # the copies and scales of the next slice have landed; the prefetch (issued last: loads complete
-    # in order) stays in flight
-    e.emit("s_waitcnt vmcnt(1) lgkmcnt(0)")
+    e.emit("s_waitcnt vmcnt(0) lgkmcnt(0)")
     e.emit("s_barrier")
     assert not e.pending
     return e.lines
@@ -288,11 +275,8 @@ def gen_mxscale():
 
 def gen_tail(col):
     """After the last slice: promote the carried tile-7 product (padding kept for a block
-    boundary the generator cannot see); WGRAD first waits for the last slice's prefetch, so no
-    load is in flight once the K loop is done."""
+    boundary the generator cannot see)."""
     e = Emitter()
-    if col:
-        e.emit("s_waitcnt vmcnt(0)")
     e.nops(HAZARD_WAIT_STATES)
     if col:
         e.fma_col(7, P_ODD, "sap")
