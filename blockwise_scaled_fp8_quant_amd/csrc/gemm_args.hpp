@@ -73,15 +73,12 @@ __host__ __device__ inline void block_of(int b, int tiles_m, int tiles_n, int sp
 // apart by tile column mod n_a), a B panel by its tiles of one tile column (n_b, by tile row mod
 // n_b).  So of each run of n lanes (n = n_a or n_b) only one row is fetched, the one whose class
 // is the tile's: the lanes of the run all point at it and their requests merge into one line.
-__device__ __forceinline__ int pf_share_a(const GemmArgs& p) {
-  const int n = min(32 / p.group, p.tiles_n);
-  return n >= 8 ? 8 : n >= 4 ? 4 : n >= 2 ? 2 : 1;
+__host__ __device__ inline int pf_share(int n) { return n >= 8 ? 8 : n >= 4 ? 4 : n >= 2 ? 2 : 1; }
+__host__ __device__ inline int pf_share_a(const GemmArgs& p) {
+  return pf_share(32 / p.group < p.tiles_n ? 32 / p.group : p.tiles_n);
 }
-__device__ __forceinline__ int pf_share_b(const GemmArgs& p) {
-  const int n = min(p.group, p.tiles_m);
-  return n >= 8 ? 8 : n >= 4 ? 4 : n >= 2 ? 2 : 1;
-}
-__device__ __forceinline__ int pf_row(int lane, int tile, int n) { return (lane & ~(n - 1)) + (tile & (n - 1)); }
+__host__ __device__ inline int pf_share_b(const GemmArgs& p) { return pf_share(p.group < p.tiles_m ? p.group : p.tiles_m); }
+__host__ __device__ inline int pf_row(int lane, int tile, int n) { return (lane & ~(n - 1)) + (tile & (n - 1)); }
 
 hipError_t launch_w4(const GemmArgs& a, bool out_bf16, hipStream_t st);
 // Whether launch_w4 can take these arguments: its operand offsets are 32-bit buffer offsets.

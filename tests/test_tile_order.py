@@ -6,6 +6,8 @@ splits and group sizes and checks that the order is a bijection of the launch gr
 that it keeps the locality it is for: the workgroups the dispatcher places on one XCD (workgroup b
 on XCD b % 8) share one split wherever the grid allows it, and on the layer sweep's WGRAD launches
 the 32 workgroups an XCD runs at once touch at most 12 operand panels (tile rows plus tile columns).
+It also checks the four-wave kernels' L2 prefetch row selection (pf_row): each lane's row stays in
+its own run of lanes, and over the tiles that share a panel every row is fetched exactly once.
 """
 import os
 import shutil
@@ -81,6 +83,39 @@ int main() {
     std::printf("tiles %d x %d splits %d group %d: %d panels per XCD\n", s[0], s[1], s[2], s[3], p);
     if (p > s[4]) return 10;
   }
+  // the L2 prefetch's row selection: a lane's row stays in its own run of n lanes (so inside the
+  // wave's 64 rows), and over the n tiles that share a panel (tile classes 0 .. n - 1) every row
+  // of the wave is fetched exactly once
+  for (int n : {1, 2, 4, 8}) {
+    if (puro::pf_share(n) != n) return 20;
+    for (int base = 0; base < 64; base += n) {
+      int hits[64] = {0};
+      for (int tile = base; tile < base + n; ++tile) {
+        std::set<int> rows;
+        for (int lane = 0; lane < 64; ++lane) {
+          const int r = puro::pf_row(lane, tile, n);
+          if (r < (lane & ~(n - 1)) || r >= (lane & ~(n - 1)) + n) return 21;
+          rows.insert(r);
+        }
+        if ((int)rows.size() != 64 / n) return 22;
+        for (int r : rows) ++hits[r];
+      }
+      for (int r = 0; r < 64; ++r)
+        if (hits[r] != 1) return 23;
+    }
+  }
+  for (int v : {3, 5, 6, 7, 9, 16, 32}) {
+    const int s = puro::pf_share(v);
+    if (s > v || (s & (s - 1)) || s > 8) return 24;
+  }
+  // shares of the sweep's FWD (group 4: 8 tiles share an A panel, 4 a B panel) and WGRAD launches
+  puro::GemmArgs g{};
+  g.group = 4; g.tiles_m = 64; g.tiles_n = 16;
+  if (puro::pf_share_a(g) != 8 || puro::pf_share_b(g) != 4) return 25;
+  g.group = 8; g.tiles_m = 16; g.tiles_n = 8;
+  if (puro::pf_share_a(g) != 4 || puro::pf_share_b(g) != 8) return 26;
+  g.group = 4; g.tiles_m = 1; g.tiles_n = 2;
+  if (puro::pf_share_a(g) != 2 || puro::pf_share_b(g) != 1) return 27;
   std::printf("ok %ld cases\n", cases);
   return 0;
 }
