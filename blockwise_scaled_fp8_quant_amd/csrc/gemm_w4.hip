@@ -20,7 +20,8 @@
 //    slice's A and B rows (256 x 128 bytes each) and scales are copied into the other with
 //    buffer_load ... lds (no VGPR round trip).  The buffer resources span the tile's valid rows, so
 //    rows past M or N read as zero (half-filled edge tiles need no clamping).
-//  * Tiles are visited in the XCD-aware order of block_of (gemm_args.hpp).
+//  * Tiles are visited in the XCD-aware order of block_of (gemm_args.hpp).  Each wave also pulls
+//    the slice after next into L2, one dword per row, asking for each line once per XCD (pf_row).
 //  * The epilogue stages each wave's quadrant through LDS (bf16: all 128 rows at once; fp32, and
 //    bf16 with the fused output quantization: 64 rows at a time) and writes whole row segments
 //    with 16-byte stores.
@@ -228,8 +229,9 @@ void gemm_w4_kernel(GemmArgs p) {
   uint32_t ob0 = (uint32_t)(crow * p.ldb) + (uint32_t)((pch ^ (crow >> 1)) << 4) + k0;
   uint32_t ob1 = (uint32_t)(crow * p.ldb) + (uint32_t)((pch ^ (crow >> 1) ^ 4) << 4) + k0;
   const uint32_t osa = (uint32_t)lane * 4u;
-  // prefetch offsets: row 64 wave + lane (the wave's base row is in qa[0] / qb[0]), two slices ahead
-  // of the one being copied; the prologue prefetches the second slice
+  // prefetch offsets, two slices ahead of the one being copied (the prologue prefetches the second
+  // slice): a row of the wave's 64 (its base row is in qa[0] / qb[0]), the one row of each run of
+  // lanes that this tile fetches for the resident tiles sharing the panel (pf_row)
   uint32_t pfa = (uint32_t)(pf_row(lane, tn, pf_share_a(p)) * p.lda) + k0 + 128u;
   uint32_t pfb = (uint32_t)(pf_row(lane, tm, pf_share_b(p)) * p.ldb) + k0 + 128u;
   int ssp;                                         // row-scale offset of the prefetched slice

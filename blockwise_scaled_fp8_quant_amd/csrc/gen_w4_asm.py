@@ -212,10 +212,11 @@ def copy_items(stage_next):
 
 
 def prefetch_items():
-    """Loads that pull the slice after the one being copied into L2 (one dword of each of the wave's
-    64 A rows, 64 B rows and of its 64 row scales, landing in an LDS area nobody reads).  Issued after
-    the copies: loads complete in order, so waiting for the copies with vmcnt(PF_LOADS) leaves them
-    in flight."""
+    """Loads that pull the slice after the one being copied into L2 (one dword per row of the wave's
+    64 A rows, 64 B rows and 64 row scales, landing in an LDS area nobody reads; the per-lane A and B
+    offsets the kernel sets up point each run of lanes at one row, so that the tiles resident on an
+    XCD request each shared line once).  Issued after the copies: loads complete in order, so
+    waiting for the copies with vmcnt(PF_LOADS) leaves them in flight."""
     return [(f"s_mov_b32 m0, {PF_LDS}", f"buffer_load_dword v{PF['pa']}, %[rA], s{QA} offen lds"),
             (f"s_mov_b32 m0, {PF_LDS}", f"buffer_load_dword v{PF['pb']}, %[rB], s{QB} offen lds"),
             (f"s_mov_b32 m0, {PF_LDS}", "buffer_load_dword %[osa], %[rS], %[ssp] offen lds")]
